@@ -1,0 +1,73 @@
+"""CPU tests of the seeded input generator (no attention arithmetic here)."""
+
+import numpy as np
+import pytest
+
+from tiled_tensor_core_amd import synth
+
+
+def test_deterministic_and_streams_distinct():
+    a = synth.make_qkv(1, 2, 64, 16, "bf16", seed=0)
+    b = synth.make_qkv(1, 2, 64, 16, "bf16", seed=0)
+    c = synth.make_qkv(1, 2, 64, 16, "bf16", seed=1)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert not np.array_equal(a[0], c[0])
+    assert not np.array_equal(a[0], a[1]) and not np.array_equal(a[1], a[2])
+
+
+def test_prefix_stable():
+    """A tensor's draws depend only on (seed, tensor id) and position, so a
+    bigger tensor starts with the smaller one's values."""
+    x = synth.draw(synth.N01, 1000, 0, 2)
+    y = synth.draw(synth.N01, 101, 0, 2)
+    assert np.array_equal(x[:101], y)
+
+
+@pytest.mark.parametrize("dist,mean,std", [(synth.N01, 0.0, 1.0), (synth.N03, 0.0, 3.0),
+                                           (synth.U11, 0.0, 1 / np.sqrt(3))])
+def test_moments(dist, mean, std):
+    x = synth.draw(dist, 400_000, 0, 0).astype(np.float64)
+    assert abs(x.mean() - mean) < 0.01 * max(std, 1)
+    assert abs(x.std() - std) < 0.01 * std
+    if dist.kind == "uniform":
+        assert x.min() > -1 and x.max() < 1
+
+
+def test_bf16_round_nearest_even():
+    f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 2.0 ** 127,
+                  1.0 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    bits = synth.round_bits(f, "bf16")
+    back = synth.bits_to_f32(bits, "bf16")
+    # ties go to even: 1+2^-8 is halfway between 1 and 1+2^-7 -> 1
+    # 1+3*2^-8 is halfway between 1+2^-7 and 1+2^-6 -> 1+2^-6 (even mantissa)
+    want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0, -2.5, 2.0 ** 127, 1.0 + 2 ** -7],
+                    dtype=np.float32)
+    assert np.array_equal(back[:6], want[:6])
+    assert back[6] == np.float32(1.0 + 2 ** -7)
+    # agrees with torch's own conversion
+    import torch
+    t = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(t, bits)
+
+
+def test_fp16_round_and_widen():
+    f = np.array([0.1, -1.5, 65504.0, 1e-6], dtype=np.float32)
+    bits = synth.round_bits(f, "fp16")
+    assert np.array_equal(synth.bits_to_f32(bits, "fp16"), f.astype(np.float16).astype(np.float32))
+
+
+def test_workloads_shapes():
+    w = synth.WORKLOADS["small"]
+    q, k, v = synth.make_workload(w)
+    assert q.shape == (1, 2, 256, 64) and q.dtype == np.uint16
+    assert synth.WORKLOADS["ragged"].N % 64 != 0
+    assert abs(synth.WORKLOADS["llama"].scale - 1 / np.sqrt(128)) < 1e-15
+
+
+def test_to_torch_same_bits():
+    import torch
+    q, _, _ = synth.make_qkv(1, 1, 8, 16, "fp16", seed=3)
+    t = synth.to_torch(q, "fp16")
+    assert t.dtype == torch.float16
+    assert np.array_equal(t.view(torch.int16).numpy().view(np.uint16), q)
