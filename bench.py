@@ -1,0 +1,222 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+A step is one call of the C ABI entry point ``attn_fwd`` over one batch of
+synthetic inputs already resident in HBM: the causal B=8, H=32, N=2048,
+d=128 bf16 workload by default (the throughput target).  The run prints one
+JSON line with whole-job TFLOP/s, the MFMA roofline fraction of the kernel
+(live, from HIP events on the launch stream), and the fp64 CPU oracle timed
+on a bounded sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama] [--no-cpu-baseline]
+
+FLOPs are algorithmic: 4*B*H*N^2*d, halved when causal (masked-tile waste and
+padding are not counted).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FlashAttention fwd TFLOP/s (causal & non-causal) + % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = 2516.6          # MI355X dense bf16/fp16 MFMA
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "attn_fwd_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_llama_causal_traffic.txt")
+
+
+def flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def time_workload(attn, torch, w, causal, steps, warmup, inputs):
+    q, k, v = inputs
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream)
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": float(np.mean(per)),
+        "kernel_ms_median": float(np.median(per)),
+        "kernel_ms_min": float(per[0]),
+        "flops": flops(B, H, N, d, causal),
+    }
+
+
+def cpu_baseline(w, causal, bits, budget_s):
+    """The fp64 oracle on whole heads of the workload until ``budget_s`` of
+    CPU time has passed; FLOPs credited with the same algorithmic count."""
+    from oracle import attention_rows
+    from tiled_tensor_core_amd import synth
+
+    qb, kb, vb = bits
+    cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    heads = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    rows = np.arange(w.N)
+    with threadpool_limits(limits=cores):
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        for bh in range(w.B * w.H):
+            b, h = divmod(bh, w.H)
+            qh = synth.bits_to_f64(qb[b, h][None, None], w.dtype)
+            kh = synth.bits_to_f64(kb[b, h][None, None], w.dtype)
+            vh = synth.bits_to_f64(vb[b, h][None, None], w.dtype)
+            ts = time.perf_counter()
+            for r0 in range(0, w.N, 512):
+                attention_rows(qh, kh, vh, causal, w.scale, 0, 0, rows[r0:r0 + 512])
+            elapsed += time.perf_counter() - ts
+            heads += 1
+            if elapsed >= budget_s:
+                break
+    f = flops(1, heads, w.N, w.d, causal)
+    return {
+        "value": f / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} heads (all {w.N} rows each), fp64 numpy, "
+                  f"{elapsed:.1f} s; wall {time.perf_counter() - t0:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the other workloads (causal and non-causal) and report them")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the attention forward pass shards over "
+              "(batch, head) with no exchange, so only the one-GPU figure is measured",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tiled_tensor_core_amd import attn, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.load_library()
+    w = synth.WORKLOADS[a.workload]
+    causal = w.causal[-1]
+    print(f"[bench] generating {w.name} inputs {w.describe()}", file=sys.stderr, flush=True)
+    bits = synth.make_workload(w)
+    inputs = tuple(synth.to_torch(x, w.dtype, "cuda") for x in bits)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
+    r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs)
+    value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"attention fwd {'causal' if causal else 'non-causal'} {w.describe()}",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+            "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+        },
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+            "kernel_ms_median": round(r["kernel_ms_median"], 5),
+        },
+    }
+    if a.extra:
+        per = {}
+        for name, ow in synth.WORKLOADS.items():
+            ob = bits if name == w.name else synth.make_workload(ow)
+            oin = inputs if name == w.name else tuple(synth.to_torch(x, ow.dtype, "cuda") for x in ob)
+            for c in (False, True):
+                rr = time_workload(attn, torch, ow, c, 20, 5, oin)
+                per[f"{name} {'causal' if c else 'non-causal'}"] = round(
+                    rr["flops"] / (rr["kernel_ms_median"] * 1e-3) / 1e12, 2)
+            del oin
+            torch.cuda.empty_cache()
+            print(f"[bench] timed {name}", file=sys.stderr, flush=True)
+        out["per_workload_tflops"] = per
+    if not a.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{a.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, causal, bits, a.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward pass.
+ *
+ * Operation (TileLang tutorial "Designing high-performance GPU kernels with
+ * a high-level Python DSL via TVM: from tensor-core GEMM to FlashAttention",
+ * section on the fused FlashAttention forward kernel): for every batch b and
+ * head h,
+ *
+ *     O   = softmax(scale * Q K^T  [+ causal mask]) V
+ *     LSE = log(sum_j exp(scale * q_i . k_j))      (natural log, visible j only)
+ *
+ * computed tile by tile with an online softmax (running row maximum, running
+ * normalisation sum, rescaling factor), so the N x N score matrix never
+ * reaches device memory.  The same section validates the kernel against
+ * PyTorch's scaled dot-product attention, causal and non-causal; these
+ * entry points follow its semantics (equal head counts, no dropout, no bias).
+ *
+ * Arguments common to every entry point
+ * -------------------------------------
+ *   q, k, v  device pointers, read only.  Each is a contiguous [B, H, N, d]
+ *            array of 16-bit floats (bf16 or fp16, see the entry point), d
+ *            fastest: element (b, h, n, c) is at ((b*H + h)*N + n)*d + c.
+ *   o        device pointer, written: fp32 [B, H, N, d], same layout.
+ *   lse      device pointer, written: fp32 [B, H, N], natural-log
+ *            log-sum-exp of the scaled, masked scores of each query row.
+ *   B, H, N  batch, heads, sequence length (queries = keys = N), each >= 1.
+ *   d        head dimension: 64 or 128.
+ *   causal   0: every key is visible; 1: key j is visible to query i iff
+ *            j <= i.
+ *   scale    finite multiplier of the scores (1/sqrt(d) for the usual
+ *            attention); any sign, zero included.
+ *   stream   a hipStream_t passed as void* (NULL = the default stream).
+ *
+ * Ownership and execution: the caller allocates and owns every buffer; the
+ * library allocates nothing and keeps no pointer after it returns.  The call
+ * only enqueues work on `stream` and returns; buffers must stay alive until
+ * that stream has finished it.  Every row n < N of o and lse is overwritten.
+ * o and lse must not overlap each other or the inputs.
+ *
+ * Alignment: every pointer must be 16-byte aligned.
+ *
+ * Errors: arguments are checked on the host before any HIP call; a failed
+ * check returns its code and touches nothing.  ATTN_ERR_HIP means the launch
+ * itself failed; attn_last_error() then returns the HIP error text for the
+ * calling thread.  The functions are stateless and may be called from
+ * several threads at once.
+ */
+#ifndef TTC_ATTN_H
+#define TTC_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,           /* a pointer argument is NULL                     */
+  ATTN_ERR_SHAPE = 2,          /* B, H or N < 1, or B*H*N*d too large            */
+  ATTN_ERR_UNSUPPORTED_D = 3,  /* d is not 64 or 128                             */
+  ATTN_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned               */
+  ATTN_ERR_DTYPE = 5,          /* dtype code is not ATTN_BF16 or ATTN_FP16       */
+  ATTN_ERR_HIP = 6,            /* the kernel launch failed (see attn_last_error) */
+  ATTN_ERR_SCALE = 7,          /* scale is NaN or infinite                       */
+  ATTN_ERR_CAUSAL = 8,         /* causal is not 0 or 1                           */
+  ATTN_ERR_ALIAS = 9           /* o or lse overlaps another buffer               */
+};
+
+enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
+
+/* Attention forward on bf16 q, k, v (FlashAttention section of the TileLang
+ * tutorial).  Returns an attn_status code. */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse,
+                  int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/* The same on fp16 q, k, v. */
+int attn_fwd_fp16(const void* q, const void* k, const void* v, float* o, float* lse,
+                  int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/* The same, with the element type of q, k, v given by `dtype`
+ * (ATTN_BF16 or ATTN_FP16). */
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int H, int N, int d, int causal, float scale, void* stream, int dtype);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* attn_status_str(int status);
+
+/* Text of the last HIP error a call on this thread returned ATTN_ERR_HIP
+ * for ("" if none).  Valid until the next call on this thread. */
+const char* attn_last_error(void);
+
+/* Query rows one workgroup of the kernel handles for head dim d (0 if d is
+ * unsupported); the grid has B*H*ceil(N / rows) workgroups. */
+int attn_block_rows(int d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTC_ATTN_H */

@@ -12,3 +12,12 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: takes more than a few seconds")
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library when it is absent (hipcc cross-compiles without a
+    GPU).  A present library is used as is: rebuild after changing a source."""
+    from tiled_tensor_core_amd import attn, build
+
+    if not os.path.exists(attn.LIB_PATH):
+        build.build()

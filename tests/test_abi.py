@@ -1,0 +1,115 @@
+"""CPU tests of the C ABI: the library loads, exports what include/attn.h
+declares, and rejects every invalid argument on the host with its status
+code before any HIP call (so no GPU is needed)."""
+
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiled_tensor_core_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# fake, 16-byte-aligned, well separated "device" addresses: validation never
+# dereferences them, and every case below fails validation
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, causal=0, scale=0.125)
+
+
+def _call(fn="attn_fwd", dtype=0, **over):
+    a = dict(GOOD)
+    a.update(over)
+    lib = attn.load_library()
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+            a["causal"], a["scale"], None)
+    if fn == "attn_fwd":
+        return lib.attn_fwd(*args, dtype)
+    return getattr(lib, fn)(*args)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    """The offload bundle of our own build names gfx950 and nothing else."""
+    data = open(attn.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"hipv4-amdgcn-amd-amdhsa-[-a-z0-9:+]*", data))
+    assert targets == {b"hipv4-amdgcn-amd-amdhsa--gfx950"}
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 16, H=1 << 16), 2),
+    (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
+    (dict(q=Q + 8), 4), (dict(o=O + 4), 4), (dict(lse=L + 2), 4),
+    (dict(scale=math.nan), 7), (dict(scale=math.inf), 7), (dict(scale=-math.inf), 7),
+    (dict(scale=3.0e38), 7),
+    (dict(causal=2), 8), (dict(causal=-1), 8),
+    (dict(o=Q), 9), (dict(lse=V + 16), 9), (dict(lse=O + 64), 9),
+])
+def test_rejects_invalid_arguments(fn, over, code):
+    assert _call(fn, **over) == code
+
+
+def test_rejects_unknown_dtype():
+    assert _call("attn_fwd", dtype=2) == 5
+    assert _call("attn_fwd", dtype=-1) == 5
+
+
+def test_status_strings():
+    lib = attn.load_library()
+    seen = set()
+    for code in attn.STATUS:
+        s = attn.attn_status_str(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == len(attn.STATUS)
+    assert attn.attn_status_str(99) == "unknown status"
+    assert lib.attn_last_error() == b""
+
+
+def test_block_rows():
+    assert attn.attn_block_rows(64) > 0 and attn.attn_block_rows(128) > 0
+    assert attn.attn_block_rows(96) == 0
+
+
+def test_binding_raises_named_error():
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_fwd(Q, K, V, O, L, 2, 3, 100, 96, 0, 0.1, stream=0, dtype=0)
+    assert e.value.code == 3 and e.value.name == "ATTN_ERR_UNSUPPORTED_D"
+    with pytest.raises(TypeError):
+        attn.attn_fwd(Q, K, V, O, L, 2, 3, 100, 64, 0, 0.1, stream=0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+
+    mod = importlib.reload(attn)
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        importlib.reload(attn)

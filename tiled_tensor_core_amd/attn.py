@@ -1,0 +1,177 @@
+"""Python binding of the C ABI in include/attn.h (ctypes; marshalling only).
+
+Every step of the attention forward pass runs in the HIP library
+``libttc_attn.so``; this module only turns tensors into pointers, sizes and
+a stream handle.  There is no fallback: if the library has not been built,
+or a call is rejected, an exception says so.
+
+Entry points (same names as the C functions):
+
+* ``attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None)``
+* ``attn_fwd_bf16(...)`` / ``attn_fwd_fp16(...)`` (same arguments, no dtype)
+* ``attn_status_str(code)``, ``attn_last_error()``, ``attn_block_rows(d)``
+
+``q, k, v, o, lse`` are torch tensors on the GPU (or raw device addresses as
+ints).  ``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` int, or
+None for torch's current stream on the tensors' device.
+
+``fwd(q, k, v, causal, scale)`` allocates ``o`` (fp32) and ``lse`` (fp32)
+with torch and calls ``attn_fwd``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttc_attn.so")
+
+ATTN_BF16 = 0
+ATTN_FP16 = 1
+
+STATUS = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_NULL",
+    2: "ATTN_ERR_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED_D",
+    4: "ATTN_ERR_ALIGN",
+    5: "ATTN_ERR_DTYPE",
+    6: "ATTN_ERR_HIP",
+    7: "ATTN_ERR_SCALE",
+    8: "ATTN_ERR_CAUSAL",
+    9: "ATTN_ERR_ALIAS",
+}
+
+EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_status_str",
+           "attn_last_error", "attn_block_rows"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+        super().__init__(f"{self.name}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m tiled_tensor_core_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_void_p]
+    for name in ("attn_fwd_bf16", "attn_fwd_fp16"):
+        fn = getattr(lib, name)
+        fn.argtypes = fwd_args
+        fn.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = fwd_args + [ctypes.c_int]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_block_rows.argtypes = [ctypes.c_int]
+    lib.attn_block_rows.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream_handle(stream, like) -> int | None:
+    if stream is None:
+        import torch
+
+        if like is not None and hasattr(like, "device") and like.device.type == "cuda":
+            return torch.cuda.current_stream(like.device).cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(q, dtype):
+    if dtype is not None:
+        return int(dtype)
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if q.dtype == torch.float16:
+        return ATTN_FP16
+    raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        lib = load_library()
+        detail = lib.attn_status_str(code).decode()
+        if code == 6:
+            detail += ": " + lib.attn_last_error().decode()
+        raise AttnError(code, detail)
+
+
+def _args(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
+            int(causal), float(scale), _stream_handle(stream, q))
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None) -> None:
+    """Enqueue the attention forward pass (see include/attn.h)."""
+    lib = load_library()
+    if dtype is None and isinstance(q, int):
+        raise TypeError("dtype is required when q is a raw address")
+    code = _dtype_code(q, dtype)
+    _check(lib.attn_fwd(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream), code))
+
+
+def attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
+    lib = load_library()
+    _check(lib.attn_fwd_bf16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream)))
+
+
+def attn_fwd_fp16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
+    lib = load_library()
+    _check(lib.attn_fwd_fp16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream)))
+
+
+def attn_status_str(code: int) -> str:
+    return load_library().attn_status_str(int(code)).decode()
+
+
+def attn_last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def attn_block_rows(d: int) -> int:
+    return int(load_library().attn_block_rows(int(d)))
+
+
+def fwd(q, k, v, causal: bool, scale: float, stream=None):
+    """O (fp32) and LSE (fp32) for [B, H, N, d] tensors q, k, v on the GPU."""
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, B, H, N, d, bool(causal), scale, stream)
+    return o, lse

@@ -1,0 +1,122 @@
+// C ABI of the attention forward pass: argument checks, scale handling and
+// dispatch.  Every check runs on the host before any HIP call, so a rejected
+// call touches neither the device nor the HIP runtime.
+
+#include <stdint.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int run(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N,
+        int d, int causal, float scale, void* stream, int dtype) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+  if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  // B*H must fit an int; element offsets are 64-bit inside the kernel.
+  const long long bh = (long long)B * H;
+  const long long rows = bh * N;
+  if (bh > (1LL << 30) || rows > (1LL << 40) || rows * d > (1LL << 46)) return ATTN_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return ATTN_ERR_ALIGN;
+  const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4,
+               lse_bytes = (size_t)rows * 4;
+  if (overlaps(o, o_bytes, lse, lse_bytes) || overlaps(o, o_bytes, q, in_bytes) ||
+      overlaps(o, o_bytes, k, in_bytes) || overlaps(o, o_bytes, v, in_bytes) ||
+      overlaps(lse, lse_bytes, q, in_bytes) || overlaps(lse, lse_bytes, k, in_bytes) ||
+      overlaps(lse, lse_bytes, v, in_bytes))
+    return ATTN_ERR_ALIAS;
+
+  ttc::AttnParams prm{};
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k = static_cast<const uint16_t*>(k);
+  prm.v = static_cast<const uint16_t*>(v);
+  prm.o = o;
+  prm.lse = lse;
+  prm.BH = (int)bh;
+  prm.N = N;
+  // The kernel works with a positive score multiplier c = |scale| * log2(e).
+  // A negative scale negates Q instead (exact for 16-bit floats), a zero
+  // scale zeroes it; either way scale * (q . k) is unchanged.
+  const double log2e = 1.4426950408889634074;
+  if (scale > 0.0f) {
+    prm.c = (float)((double)scale * log2e);
+    prm.q_mode = 0;
+  } else if (scale < 0.0f) {
+    prm.c = (float)(-(double)scale * log2e);
+    prm.q_mode = 1;
+  } else {
+    prm.c = (float)log2e;
+    prm.q_mode = 2;
+  }
+  if (!std::isfinite(prm.c)) return ATTN_ERR_SCALE;  // |scale| * log2(e) overflows fp32
+  if (prm.c == 0.0f) {  // |scale| below fp32 range: every score rounds to 0
+    prm.c = (float)log2e;
+    prm.q_mode = 2;
+  }
+
+  hipError_t e = ttc::launch_attn_fwd(dtype == ATTN_BF16, d, causal == 1, prm,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+                  int N, int d, int causal, float scale, void* stream) {
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_BF16);
+}
+
+int attn_fwd_fp16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+                  int N, int d, int causal, float scale, void* stream) {
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_FP16);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+             int N, int d, int causal, float scale, void* stream, int dtype) {
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype);
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a pointer argument is NULL";
+    case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and B*H*N*d within limits";
+    case ATTN_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+    case ATTN_ERR_DTYPE: return "dtype must be ATTN_BF16 or ATTN_FP16";
+    case ATTN_ERR_HIP: return "kernel launch failed (see attn_last_error)";
+    case ATTN_ERR_SCALE: return "scale must be finite";
+    case ATTN_ERR_CAUSAL: return "causal must be 0 or 1";
+    case ATTN_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_block_rows(int d) { return (d == 64 || d == 128) ? ttc::block_rows(d) : 0; }
+
+}  // extern "C"

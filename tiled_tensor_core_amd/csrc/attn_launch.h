@@ -1,0 +1,28 @@
+// Internal interface between the C ABI (attn_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ttc {
+
+struct AttnParams {
+  const uint16_t* q;   // [BH, N, D] 16-bit floats
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;            // [BH, N, D]
+  float* lse;          // [BH, N]
+  int BH;              // batch * heads
+  int N;               // sequence length
+  int n_qblk;          // query blocks per head (set by the launcher)
+  int xcd_remap;       // 1: keep each head's blocks on one XCD (set by the launcher)
+  float c;             // |scale| * log2(e), or log2(e) when scale == 0
+  int q_mode;          // 0: use Q; 1: use -Q (negative scale); 2: use 0 (zero scale)
+};
+
+// Query rows per workgroup for head dim d.
+int block_rows(int d);
+
+// Enqueue the kernel on `stream`.  Arguments are already validated.
+hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, hipStream_t stream);
+
+}  // namespace ttc
