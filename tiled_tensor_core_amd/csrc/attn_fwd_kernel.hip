@@ -14,8 +14,11 @@
 //   * Q: each wave keeps its rows in VGPRs for the whole pass, as the B
 //     operand of v_mfma_f32_32x32x16 (8 consecutive head-dim elements per
 //     lane), loaded once from HBM.
-//   * K/V: BC-key tiles are staged through LDS, double buffered; the next
-//     tile's global loads are in flight while the current tile is computed.
+//   * K/V: BC-key tiles are copied HBM -> LDS with global_load_lds_dwordx4
+//     (no VGPR staging), double buffered: the next tile's loads are in
+//     flight while the current tile is computed; one barrier per tile.
+//   * two workgroups share a CU (<= 256 VGPRs per wave, 2 waves per SIMD) so
+//     one wave's softmax VALU work overlaps the other's MFMAs.
 //   * scores are computed transposed, S^T = K Q^T, so the accumulator puts
 //     one query row per lane (column = lane % 32) and 16 of its keys in the
 //     lane's registers; the other 16 keys of that row sit in lane ^ 32.  A
@@ -29,6 +32,15 @@
 //     transposed copy.
 //   * softmax in base 2: p = exp2(s*c - m*c) with c = scale*log2(e) folded
 //     into one FMA; LSE = ln2 * (m*c + log2(l)) at the end.
+//   * the running maximum m used as the exponent reference is moved (and
+//     O, l rescaled by alpha = exp2((m_old - m_new)*c)) only when some row's
+//     tile maximum exceeds it by more than a margin (in log2 units); when no
+//     row of the wave qualifies, the rescale of O is skipped.  bf16 uses a
+//     zero margin: m is the exact running maximum, so a row's largest
+//     probability is exactly 1 and survives the bf16 rounding of P without
+//     error (this matters on peaky rows).  fp16, with 8 more bits of
+//     mantissa for P, keeps a stale reference until a row outgrows it by
+//     2^8 (p <= 256).  O / l and LSE do not depend on the reference.
 //
 // LDS layout of one stage: K tile [BC][D] then V tile [BC][D], bf16/fp16,
 // rows of D*2 bytes split in 16-byte chunks.  The chunk index is XOR-swizzled
@@ -100,7 +112,7 @@ __device__ static inline float pair_sum(float x) {
 __device__ static inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool BF16, int D, int BC, int QT, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
   using O = Ops<BF16>;
   constexpr int BM = NW * 32 * QT;             // query rows per workgroup
@@ -108,17 +120,17 @@ attn_fwd_kernel(AttnParams p) {
   constexpr int ROW_BYTES = D * 2;
   constexpr int TILE_BYTES = BC * ROW_BYTES;   // one K or V tile
   constexpr int NT = NW * 64;                  // threads per workgroup
-  constexpr int PER_T = BC * CPR / NT;         // 16-byte chunks per thread per tile
+  constexpr int PER_W = BC * CPR / 64 / NW;    // 1 KiB direct loads per wave per tile
   constexpr int KB = BC / 32;                  // 32-key blocks per tile
   constexpr int DK = D / 16;                   // k-steps of the score product
   constexpr int DT = D / 32;                   // 32-wide head-dim blocks of O
-  static_assert(BC * CPR % NT == 0, "tile must split evenly over the threads");
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.N;
 
   // ---- workgroup -> (head, query block) ----------------------------------
@@ -165,29 +177,27 @@ attn_fwd_kernel(AttnParams p) {
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  // ---- K/V tile staging ---------------------------------------------------
-  u32x4 kst[PER_T], vst[PER_T];
-  auto load_tile = [&](int j) {
+  // ---- K/V tile loads: HBM -> LDS directly ----------------------------------
+  // One global_load_lds_dwordx4 moves 64 lanes x 16 bytes into 1 KiB of LDS,
+  // lane l landing at base + 16*l.  LDS chunk index idx = row*CPR + slot, so
+  // lane l of load t fetches the global chunk that the swizzle puts in that
+  // slot.  Rows past the end repeat the last row: finite values whose scores
+  // are masked, so they add exactly 0.
+  auto issue_tile = [&](int j, int stage) {
+    uint8_t* kdst = smem + stage * 2 * TILE_BYTES;
+    uint8_t* vdst = kdst + TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int id = threadIdx.x + i * NT;
-      const int r = id / CPR, c = id % CPR;
-      // rows past the end repeat the last row: finite values whose scores
-      // are masked, so they add exactly 0
+    for (int t = 0; t < PER_W; ++t) {
+      const int blk = wave * PER_W + t;            // 1 KiB block of the tile
+      const int idx = blk * 64 + lane;             // LDS chunk index
+      const int r = idx / CPR, slot = idx % CPR;
       const int grow = min(j * BC + r, N - 1);
-      kst[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)grow * D + c * 8);
-      vst[i] = *reinterpret_cast<const u32x4*>(vh + (size_t)grow * D + c * 8);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint8_t* kbase = smem + stage * 2 * TILE_BYTES;
-    uint8_t* vbase = kbase + TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int id = threadIdx.x + i * NT;
-      const int r = id / CPR, c = id % CPR;
-      *reinterpret_cast<u32x4*>(kbase + r * ROW_BYTES + ((c ^ (r & 7)) << 4)) = kst[i];
-      *reinterpret_cast<u32x4*>(vbase + r * ROW_BYTES + ((c ^ (2 * (r & 3))) << 4)) = vst[i];
+      const uint16_t* krow = kh + (size_t)grow * D;
+      const uint16_t* vrow = vh + (size_t)grow * D;
+      __builtin_amdgcn_global_load_lds(krow + ((slot ^ (r & 7)) << 3),
+                                       (__attribute__((address_space(3))) void*)(kdst + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vrow + ((slot ^ (2 * (r & 3))) << 3),
+                                       (__attribute__((address_space(3))) void*)(vdst + blk * 1024), 16, 0, 0);
     }
   };
 
@@ -212,13 +222,18 @@ attn_fwd_kernel(AttnParams p) {
   const int vkey = 4 * (g >> 1) + (gj >> 2);    // + 32*kb + 16*h (and + 8)
   const int vcol = 16 * (g & 1) + 4 * (gj & 3); // + 32*t (head-dim column)
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  issue_tile(0, 0);
+  // raw-score margin before m moves (finite even for a tiny c)
+  constexpr float RESCALE_LOG2 = BF16 ? 0.0f : 8.0f;
+  const float thr = fminf(RESCALE_LOG2 / c, 3.0e38f);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int stage = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    // this wave's loads of tile j have landed; the barrier makes every
+    // wave's loads visible and ends every wave's use of the other buffer
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
     const int c0 = j * BC;
     const uint8_t* kbase = smem + stage * 2 * TILE_BYTES;
     const uint8_t* vbase = kbase + TILE_BYTES;
@@ -267,11 +282,21 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][kb][r]);
         mx = pair_max(mx);
-        const float mnew = fmaxf(m[qt], mx);
-        // no visible key yet in this row: keep every factor finite
-        const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-        const float mc = muse * c;
-        const float alpha = fast_exp2(m[qt] * c - mc);
+        // move the reference only when some row outgrew it by the margin
+        // (always on the first tile, where m is -inf)
+        if (__builtin_amdgcn_ballot_w64(mx > m[qt] + thr) != 0) {
+          const float mnew = fmaxf(m[qt], mx);
+          // a row with no visible key yet keeps every factor finite
+          const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
+          const float alpha = fast_exp2((m[qt] - mref) * c);   // 0 while m is -inf
+          l[qt] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qt][t][r] *= alpha;
+          m[qt] = mnew;
+        }
+        const float mc = ((m[qt] == -INFINITY) ? 0.0f : m[qt]) * c;
         float rs = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -281,12 +306,7 @@ attn_fwd_kernel(AttnParams p) {
             s[qt][kb][r] = pv;
             rs += pv;
           }
-        l[qt] = alpha * l[qt] + rs;
-        m[qt] = mnew;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qt][t][r] *= alpha;
+        l[qt] += rs;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -319,8 +339,6 @@ attn_fwd_kernel(AttnParams p) {
       }
     }
 
-    if (j + 1 < n_tiles) store_tile(stage ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m*c + log2 l) -----------------
