@@ -33,6 +33,8 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   const long long bh = (long long)B * H;
   const long long rows = bh * N;
   if (bh > (1LL << 30) || rows > (1LL << 40) || rows * d > (1LL << 46)) return ATTN_ERR_SHAPE;
+  // one head's K or V is addressed with 32-bit byte offsets
+  if ((long long)N * d * 2 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return ATTN_ERR_ALIGN;
   const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4,
