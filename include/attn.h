@@ -55,7 +55,9 @@ extern "C" {
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,           /* a pointer argument is NULL                     */
-  ATTN_ERR_SHAPE = 2,          /* B, H or N < 1, or B*H*N*d too large            */
+  ATTN_ERR_SHAPE = 2,          /* B, H or N < 1, B*H*N*d too large, or one head's
+                                  fp32 O with 128 rows of margin,
+                                  (N + 128) * d * 4 bytes, above 2^32 - 1      */
   ATTN_ERR_UNSUPPORTED_D = 3,  /* d is not 64 or 128                             */
   ATTN_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned               */
   ATTN_ERR_DTYPE = 5,          /* dtype code is not ATTN_BF16 or ATTN_FP16       */
@@ -88,8 +90,9 @@ const char* attn_status_str(int status);
  * for ("" if none).  Valid until the next call on this thread. */
 const char* attn_last_error(void);
 
-/* Query rows one workgroup of the kernel handles for head dim d (0 if d is
- * unsupported); the grid has B*H*ceil(N / rows) workgroups. */
+/* Query rows of one work item of the kernel for head dim d (0 if d is
+ * unsupported): there are B*H*ceil(N / rows) items, which the kernel's
+ * workgroups (as many as the device runs at once) share out. */
 int attn_block_rows(int d);
 
 #ifdef __cplusplus

@@ -62,6 +62,8 @@ def test_library_is_built_for_gfx950():
 @pytest.mark.parametrize("over,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 16, H=1 << 16), 2),
+    # one head's fp32 O plus 128 rows must stay within 32-bit byte offsets
+    (dict(B=1, H=1, N=(1 << 23) - 128, d=128), 2), (dict(B=1, H=1, N=(1 << 24) - 128, d=64), 2),
     (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
     (dict(q=Q + 8), 4), (dict(o=O + 4), 4), (dict(lse=L + 2), 4),
     (dict(scale=math.nan), 7), (dict(scale=math.inf), 7), (dict(scale=-math.inf), 7),

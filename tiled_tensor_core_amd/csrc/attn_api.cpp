@@ -33,8 +33,9 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   const long long bh = (long long)B * H;
   const long long rows = bh * N;
   if (bh > (1LL << 30) || rows > (1LL << 40) || rows * d > (1LL << 46)) return ATTN_ERR_SHAPE;
-  // one head's K or V is addressed with 32-bit byte offsets
-  if ((long long)N * d * 2 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  // one head's K, V or O is addressed with 32-bit byte offsets (O: fp32,
+  // with room for the rows of a ragged last block of 128)
+  if ((long long)(N + 128) * d * 4 > 0xffffffffLL) return ATTN_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return ATTN_ERR_ALIGN;
   const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4,

@@ -9,9 +9,13 @@
 // cores.
 //
 // Work split and data flow (all of it designed for CDNA4):
-//   * workgroup = 4 waves; wave w owns 32 query rows, the workgroup 128 rows
-//     of one (batch, head).  Two workgroups share a CU (<= 256 VGPRs per
-//     wave, 64 KiB of LDS each), so every SIMD runs two waves.
+//   * an item is 128 query rows of one (batch, head); workgroup = 4 waves,
+//     wave w owns 32 of the item's rows.  Two workgroups share a CU (<= 256
+//     VGPRs per wave, 64 KiB of LDS each), so every SIMD runs two waves.
+//   * the kernel is persistent: the grid is as many workgroups as the chip
+//     holds at once, each working through a fixed list of items (see the
+//     item order in the kernel).  While an item's last tile is finished,
+//     the next item's Q and first K/V tiles are already being loaded.
 //   * Q: each wave keeps its 32 rows in VGPRs for the whole pass, as the B
 //     operand of v_mfma_f32_32x32x16 (8 consecutive head-dim elements per
 //     lane), loaded once from HBM.
@@ -40,9 +44,11 @@
 //     ds_read_b64_tr_b16 (gfx950 transposing LDS read), so V never needs a
 //     transposed copy.
 //   * tiles that need a mask (causal diagonal, keys past N) are the last
-//     one or two of every workgroup; they run after the pipelined loop in a
-//     plain loop that masks, and tiles wholly above a wave's rows are
-//     skipped there (causal tile skipping).
+//     one or two of every item; they run after the pipelined loop in a
+//     loop that masks, and tiles wholly above a wave's rows are skipped
+//     there (causal tile skipping).
+//   * O leaves through LDS: each wave turns its accumulators row-major in
+//     4 KiB of LDS so every store writes whole 128-byte row pieces.
 //   * softmax in base 2: p = exp2(s*c - m*c) with c = scale*log2(e) folded
 //     into one FMA; LSE = ln2 * (m*c + log2(l)) at the end.
 //   * the running maximum m used as the exponent reference moves (and O, l
@@ -68,6 +74,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -86,6 +94,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 #define TTC_INLINE __device__ __attribute__((always_inline)) inline
 
@@ -160,6 +169,7 @@ constexpr int kNW = 4;         // waves per workgroup
 constexpr int kBM = kNW * 32;  // query rows per workgroup
 constexpr int kLead = 3;       // LDS operand reads issued this many MFMAs ahead
 constexpr int kChunks = 16;    // VALU slices per phase of a pipelined tile
+constexpr int kLoadEvery = 2;  // a pipelined tile issues one K/V tile load every this many steps
 
 // Per-wave state and the work of one key tile.
 template <bool BF16, int D>
@@ -185,15 +195,15 @@ struct Wave {
   float alpha;       // pending rescale factor of O and l for the current tile
   float mc;          // m * c, the exponent offset of the current tile
   bool moved;        // some row of the wave moved its reference maximum (alpha != 1)
-  int kro[DK];       // LDS byte address of this lane's K operand (buffer 0)
-  int vro[DT];       // LDS byte address of this lane's V^T operand (buffer 0)
+  int kro[DK];       // byte offset of this lane's K operand in a K tile, per k-step
+  int vro[DT];       // byte offset of this lane's V^T operand in a V tile, per d-block
 
   TTC_INLINE static float at(const f32x16 (&s)[KB], int v) { return s[v >> 4][v & 15]; }
 
   // ---- MFMA steps -------------------------------------------------------------
   // Score step i (kk = i / KB, kb = i % KB): S^T[kb] += K[kb-th 32 keys][kk] Q^T.
-  TTC_INLINE u32x4 kop(int i, int kbuf) const {
-    return *lds_at<u32x4>(kro[i / KB] + kbuf + (i % KB) * 32 * ROW_BYTES);
+  TTC_INLINE u32x4 kop(int i, const lds_u8* kt) const {
+    return *(const __attribute__((address_space(3))) u32x4*)(kt + kro[i / KB] + (i % KB) * 32 * ROW_BYTES);
   }
   TTC_INLINE void qk(int i, u32x4 a, f32x16 (&s)[KB]) const {
     const int kk = i / KB, kb = i % KB;
@@ -201,11 +211,12 @@ struct Wave {
   }
   // P V step i (t = i / (2 KB), kb = (i / 2) % KB, h = i % 2):
   // O^T[t] += V^T[t-th 32 dims][16 keys] P^T[16 keys].
-  TTC_INLINE u32x4 vop(int i, int vbuf) const {
+  TTC_INLINE u32x4 vop(int i, const lds_u8* vt) const {
     const int t = i / (2 * KB), kb = (i / 2) % KB, h = i % 2;
-    const int pa = vro[t] + vbuf + (kb * 32 + 16 * h) * ROW_BYTES;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<i16x4>(pa));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<i16x4>(pa + 8 * ROW_BYTES));
+    const lds_u8* pa = vt + vro[t] + (kb * 32 + 16 * h) * ROW_BYTES;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * ROW_BYTES));
     return (u32x4){__builtin_bit_cast(uint32_t, (i16x2){lo[0], lo[1]}),
                    __builtin_bit_cast(uint32_t, (i16x2){lo[2], lo[3]}),
                    __builtin_bit_cast(uint32_t, (i16x2){hi[0], hi[1]}),
@@ -264,12 +275,12 @@ struct Wave {
   }
 
   // ---- one tile without pipelining (masked tiles, short sequences) ----------
-  TTC_INLINE void scores(f32x16 (&s)[KB], int kbuf) const {
+  TTC_INLINE void scores(f32x16 (&s)[KB], const lds_u8* kt) const {
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) qk(i, kop(i, kbuf), s);
+    for (int i = 0; i < NQK; ++i) qk(i, kop(i, kt), s);
   }
   // O = alpha O + P V for the tile in s, whose maximum is already applied.
-  TTC_INLINE void finish(f32x16 (&s)[KB], int vbuf) {
+  TTC_INLINE void finish(f32x16 (&s)[KB], const lds_u8* vt) {
 #pragma unroll
     for (int v = 0; v < NS; ++v) prob(s, v);
 #pragma unroll
@@ -278,12 +289,12 @@ struct Wave {
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) pv(i, vop(i, vbuf));
+    for (int i = 0; i < NPV; ++i) pv(i, vop(i, vt));
   }
 
   // ---- one pipelined tile ------------------------------------------------------
   // On entry s holds tile j's scores with m, mc, alpha already set for it;
-  // K buffer KBUF holds tile j+1's keys and V buffer VBUF tile j's values.
+  // kt holds tile j+1's keys and vt tile j's values.
   // On exit sn holds tile j+1's scores, m/mc/alpha are set for tile j+1, and
   // O, l include tile j.
   //   phase 1 (NQK steps, MFMA: scores of tile j+1 into sn), VALU slices:
@@ -295,12 +306,18 @@ struct Wave {
   //     level; 12: third; 13: rest, l = alpha l + sum; 12-14: maximum tree
   //     of tile j+1; 15: new reference maximum, alpha, mc of tile j+1
   // RESCALE = false is the variant for tiles whose alpha is exactly 1.
-  template <int KBUF, int VBUF, bool RESCALE>
-  TTC_INLINE void pipe_tile(f32x16 (&s)[KB], f32x16 (&sn)[KB]) {
+  // ld(k), k = 0 .. NLOAD-1, issues this wave's k-th load of the tiles the
+  // step prefetches; the loads are spread over the first steps so their LDS
+  // writes do not all land with the tile's first reads.
+  // MAXN = false leaves tile j+1's maximum (and m, mc, alpha) to the caller,
+  // for a next tile that must be masked first.
+  template <bool RESCALE, int NLOAD, class LD, bool MAXN = true>
+  TTC_INLINE void pipe_tile(f32x16 (&s)[KB], f32x16 (&sn)[KB], const lds_u8* kt, const lds_u8* vt,
+                            const LD& ld) {
     constexpr int L = kLead, NSTEP = NQK + NPV;
     u32x4 op[L];
 #pragma unroll
-    for (int g = 0; g < L; ++g) op[g] = kop(g, KBUF);
+    for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
     float rs[NS / 2];
     float mp[11], q[4];
 #pragma unroll
@@ -308,11 +325,12 @@ struct Wave {
       const bool p1 = g < NQK;
       const int i = p1 ? g : g - NQK;
       const u32x4 a = op[g % L];
-      if (g + L < NSTEP) op[g % L] = (g + L < NQK) ? kop(g + L, KBUF) : vop(g + L - NQK, VBUF);
+      if (g + L < NSTEP) op[g % L] = (g + L < NQK) ? kop(g + L, kt) : vop(g + L - NQK, vt);
       if (p1)
         qk(i, a, sn);
       else
         pv(i, a);
+      if (g % kLoadEvery == 0 && g / kLoadEvery < NLOAD) ld(g / kLoadEvery);
       const int n_steps = p1 ? NQK : NPV;
       const int c_lo = i * kChunks / n_steps, c_hi = (i + 1) * kChunks / n_steps;
 #pragma unroll
@@ -344,15 +362,20 @@ struct Wave {
           } else if (cc == 12) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) rs[k] = rs[2 * k] + rs[2 * k + 1];
+            if (MAXN) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-              mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+              for (int k = 0; k < 4; ++k)
+                mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+            }
           } else if (cc == 13) {
             rs[0] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
             l = RESCALE ? __builtin_fmaf(l, alpha, rs[0]) : l + rs[0];
+            if (MAXN) {
 #pragma unroll
-            for (int k = 4; k < 8; ++k)
-              mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+              for (int k = 4; k < 8; ++k)
+                mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+            }
+          } else if (!MAXN) {
           } else if (cc == 14) {
             mp[8] = fmaxf(fmaxf(at(sn, 24), at(sn, 25)), at(sn, 26));
             mp[9] = fmaxf(fmaxf(at(sn, 27), at(sn, 28)), at(sn, 29));
@@ -375,11 +398,25 @@ struct Wave {
 // LDS at dst: PER_W buffer_load_dwordx4 ... lds, lane offsets off[] within
 // the tile.  Rows of the tile past N (only in the last tile) are clamped to
 // row N-1, keeping the swizzled slot of the row they stand in for.
+TTC_INLINE void load_one(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, int off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, soff, 0, 0);
+}
+
 template <int PER_W, int ROW_BYTES, int BC>
-TTC_INLINE void load_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, const int* off, int j) {
+TTC_INLINE void load_tile(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, const int* off, int j) {
 #pragma unroll
   for (int t = 0; t < PER_W; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + t * 1024), 16, off[t], j * BC * ROW_BYTES, 0, 0);
+}
+
+// Buffer resource spanning nbytes from base (one head's K, V or O); loads
+// outside it return 0, stores outside it are dropped.
+TTC_INLINE __amdgpu_buffer_rsrc_t head_rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+TTC_INLINE void store_b128(__amdgpu_buffer_rsrc_t rs, f32x4 v, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 0);
 }
 
 template <bool BF16, int D, bool CAUSAL>
@@ -396,230 +433,345 @@ attn_fwd_kernel(AttnParams p) {
   static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
   static_assert(4 * TILE_BYTES <= 65536, "LDS offsets must fit the instruction offset field");
 
-  // K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
+  // two K and two V tile buffers, each its own LDS object: the compiler can
+  // then tell that a direct-to-LDS load into one buffer does not touch the
+  // buffer being read, and need not wait for the load before reading
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE_BYTES];
+  lds_u8* const K0 = (lds_u8*)k_lds0;
+  lds_u8* const K1 = (lds_u8*)k_lds1;
+  lds_u8* const V0 = (lds_u8*)v_lds0;
+  lds_u8* const V1 = (lds_u8*)v_lds1;
+  // d = 64: a separate 16 KiB for turning O row-major before it is stored
+  // (d = 128 uses the V buffer the last tile read; see the epilogue)
+  constexpr int STAGE_BYTES = D == 64 ? 4 * 4096 : 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t o_lds[STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.N;
+  const unsigned HEAD_BYTES = (unsigned)N * ROW_BYTES;
 
-  // ---- workgroup -> (head, query block) ----------------------------------
-  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  When the
-  // head count allows, all query blocks of one head go to the same XCD so its
-  // K/V stay in that XCD's L2; causal runs take the longest blocks first.
+  // ---- work items ------------------------------------------------------------
+  // An item is one (head, query block).  The grid holds only as many
+  // workgroups as the chip runs at once, and each one works through a fixed
+  // list of items, so no workgroup waits to be dispatched and the last wave
+  // of work is not left to chance.  Workgroups are dispatched round-robin
+  // over the 8 XCDs (id % 8); when the head count allows, the heads are split
+  // into 8 equal domains, one per XCD, so a head's K/V stay in one L2.  A
+  // domain's items are listed group by group (gh heads per group), longest
+  // first within a group (causal blocks further down the sequence see more
+  // keys), and dealt out in rounds of one item per workgroup, the direction
+  // of the deal alternating between rounds: over two rounds each workgroup
+  // gets a long item and a short one whose costs add up to about the same.
   const int nq = p.n_qblk;
-  int bh, qb;
-  {
-    const int id = blockIdx.x;
-    if (p.xcd_remap) {
-      const int xcd = id & 7, slot = id >> 3;
-      bh = xcd * (p.BH >> 3) + slot / nq;
-      qb = slot % nq;
-    } else {
-      bh = id / nq;
-      qb = id % nq;
-    }
-    if (CAUSAL) qb = nq - 1 - qb;
-  }
-  const int q0 = qb * BM;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const int wr0 = q0 + wave * 32;              // first query row of this wave
-  const int qrow = wr0 + (lane & 31);          // this lane's query row
+  const int dom = p.n_dom == 8 ? (int)(blockIdx.x & 7) : 0;
+  const int wk = p.n_dom == 8 ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int nw = p.n_work, hd = p.BH / p.n_dom, gh = p.grp;
+  const int dom_items = hd * nq;
+  auto item = [&](int t, int& bh, int& qb) {
+    const int pos = t * nw + ((t & 1) ? nw - 1 - wk : wk);
+    if (pos >= dom_items) return false;
+    const int g = pos / (gh * nq), k = pos - g * (gh * nq);
+    const int gs = min(gh, hd - g * gh);   // heads in this group
+    const int r = k / gs;
+    bh = dom * hd + g * gh + (k - r * gs);
+    qb = CAUSAL ? nq - 1 - r : r;
+    return true;
+  };
+  auto tiles_of = [&](int qb) { return ((CAUSAL ? min(N, qb * BM + BM) : N) + BC - 1) / BC; };
 
   W w;
-  // ---- Q fragments: lane holds Q[row = lane % 32][8*(lane/32) + 16*kk .. +7]
-  {
-    const int row = min(qrow, N - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + head_off + (size_t)row * D + 8 * (lane >> 5));
+  // ---- Q fragments: lane holds Q[row = lane % 32][8*(lane/32) + 16*kk .. +7].
+  // Plain loads into the fragment registers; the sign fix for a negative or
+  // zero scale is applied once they have landed.
+  auto load_q = [&](int bh, int qb) {
+    const int row = min(qb * BM + wave * 32 + (lane & 31), N - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + (size_t)bh * N * D + (size_t)row * D + 8 * (lane >> 5));
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-      u32x4 x = src[2 * kk];
-      if (p.q_mode == 1) x ^= 0x80008000u;         // negative scale: flip every sign
-      if (p.q_mode == 2) x = (u32x4){0, 0, 0, 0};  // zero scale
-      w.qf[kk] = x;
-    }
-  }
+    for (int kk = 0; kk < DK; ++kk) w.qf[kk] = src[2 * kk];
+  };
 
   // ---- K/V tile loads: HBM -> LDS directly ----------------------------------
   // One buffer_load_dwordx4 ... lds moves 64 lanes x 16 bytes into 1 KiB of
   // LDS, lane l landing at base + 16*l.  LDS chunk index idx = row*CPR + slot,
   // so lane l of load t fetches the global chunk that the swizzle puts in
   // that slot.  The buffer spans the head; the tile is the scalar offset.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head_off), 0, N * ROW_BYTES, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head_off), 0, N * ROW_BYTES, 0x00020000);
+  // The per-lane offsets depend on the lane only.  They are recomputed at
+  // the start of every item (from a lane number the compiler cannot see
+  // through) rather than kept live across items, where they would only take
+  // up registers in the epilogue.
   const int first_idx = wave * PER_W * 64 + lane;   // LDS chunk index of this lane's first load
-  int koff[PER_W], voff[PER_W];
+  auto lane_offsets = [&](int ln, int (&ko)[PER_W], int (&vo)[PER_W]) {
 #pragma unroll
-  for (int t = 0; t < PER_W; ++t) {
-    const int idx = first_idx + 64 * t;
-    const int r = idx / CPR, slot = idx % CPR;
-    koff[t] = r * ROW_BYTES + ((slot ^ S::k(r)) << 4);
-    voff[t] = r * ROW_BYTES + ((slot ^ S::v(r)) << 4);
-  }
+    for (int t = 0; t < PER_W; ++t) {
+      const int idx = wave * PER_W * 64 + ln + 64 * t;
+      const int r = idx / CPR, slot = idx % CPR;
+      ko[t] = r * ROW_BYTES + ((slot ^ S::k(r)) << 4);
+      vo[t] = r * ROW_BYTES + ((slot ^ S::v(r)) << 4);
+    }
+  };
+  int koff[PER_W], voff[PER_W];
+  lane_offsets(lane, koff, voff);
   // The last tile's rows past N (if any) repeat row N-1 (finite values whose
   // scores are masked, so they add exactly 0), keeping the swizzled slot of
   // the row they stand in for.
   const int j_tail = (N - 1) / BC;
-  auto tail_off = [&](const int (&off)[PER_W], int (&o)[PER_W]) {
+  auto tail_delta = [&](int t) {
+    // recomputed where used: kept live, these would only take up registers
+    int fi = first_idx;
+    asm volatile("" : "+v"(fi));
+    const int r = (fi + 64 * t) / CPR;
+    return (min(r, N - 1 - j_tail * BC) - r) * ROW_BYTES;
+  };
+  const int wofs = wave * PER_W * 1024;   // this wave's share of a tile
+  auto load_kv = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[PER_W], lds_u8* buf, int j) {
+    if (j == j_tail) {
+      int o[PER_W];
 #pragma unroll
-    for (int t = 0; t < PER_W; ++t) {
-      const int r = (first_idx + 64 * t) / CPR;
-      o[t] = off[t] + (min(r, N - 1 - j_tail * BC) - r) * ROW_BYTES;
-    }
-  };
-  uint8_t* const kdst = smem + wave * PER_W * 1024;                   // + buf * TILE_BYTES
-  uint8_t* const vdst = smem + 2 * TILE_BYTES + wave * PER_W * 1024;  // + buf * TILE_BYTES
-  auto load_k = [&](int j) {
-    if (j == j_tail) {
-      int o[PER_W];
-      tail_off(koff, o);
-      load_tile<PER_W, ROW_BYTES, BC>(krs, kdst + (j & 1) * TILE_BYTES, o, j);
+      for (int t = 0; t < PER_W; ++t) o[t] = off[t] + tail_delta(t);
+      load_tile<PER_W, ROW_BYTES, BC>(rs, buf + wofs, o, j);
     } else {
-      load_tile<PER_W, ROW_BYTES, BC>(krs, kdst + (j & 1) * TILE_BYTES, koff, j);
-    }
-  };
-  auto load_v = [&](int j) {
-    if (j == j_tail) {
-      int o[PER_W];
-      tail_off(voff, o);
-      load_tile<PER_W, ROW_BYTES, BC>(vrs, vdst + (j & 1) * TILE_BYTES, o, j);
-    } else {
-      load_tile<PER_W, ROW_BYTES, BC>(vrs, vdst + (j & 1) * TILE_BYTES, voff, j);
+      load_tile<PER_W, ROW_BYTES, BC>(rs, buf + wofs, off, j);
     }
   };
 
-  // ---- per-lane LDS read addresses (buffer 0; buffer 1 is + TILE_BYTES) -------
-  {
-    const int lds0 = (int)(uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)smem;
-    const int krow = lane & 31;                   // key row within a 32-key block
-    const int kchunk = lane >> 5;                 // + 2*kk
+  // ---- per-lane LDS read offsets within a tile ------------------------------------
+  auto read_offsets = [&](int ln) {
+    const int krow = ln & 31;                     // key row within a 32-key block
+    const int kchunk = ln >> 5;                   // + 2*kk
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk)
-      w.kro[kk] = lds0 + krow * ROW_BYTES + (((2 * kk + kchunk) ^ S::k(krow)) << 4);
-    const int g = lane >> 4, gj = lane & 15;      // 16-lane group for the V reads
+      w.kro[kk] = krow * ROW_BYTES + (((2 * kk + kchunk) ^ S::k(krow)) << 4);
+    const int g = ln >> 4, gj = ln & 15;          // 16-lane group for the V reads
     const int vkey = 4 * (g >> 1) + (gj >> 2);    // + 32*kb + 16*h (and + 8)
     const int vcol = 16 * (g & 1) + 4 * (gj & 3); // + 32*t (head-dim column)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const int col = 32 * t + vcol;
-      w.vro[t] = lds0 + 2 * TILE_BYTES + vkey * ROW_BYTES + (((col >> 3) ^ S::v(vkey)) << 4) + ((col & 7) << 1);
+      w.vro[t] = vkey * ROW_BYTES + (((col >> 3) ^ S::v(vkey)) << 4) + ((col & 7) << 1);
     }
-  }
-
-  // ---- running state -------------------------------------------------------
+  };
   w.c = p.c;                                    // |scale| * log2(e), > 0
   w.thr = p.thr;                                // raw-score margin before m moves
-  w.m = -INFINITY;
-  w.l = 0.0f;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) w.oacc[t][r] = 0.0f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  // mask limit of tile j for this lane (see Wave::mask), and whether any row
-  // of this wave needs the mask there
-  auto mask_lim = [&](int j) { return (CAUSAL ? min(qrow, N - 1) : N - 1) - j * BC - 4 * (lane >> 5); };
-  auto needs_mask = [&](int j) { return (CAUSAL && j * BC + BC - 1 > wr0) || j * BC + BC > N; };
-  // Tiles no row of the workgroup needs masked run software-pipelined: step j
-  // handles tile j and computes tile j+1's scores and maximum, so both must
-  // be such tiles; its loads (K_{j+2}, V_{j+1}) must not reach the tile that
-  // ends past N.  The rest run in a plain loop.
-  const int n_full = CAUSAL ? min(q0 / BC, N / BC) : N / BC;
-  int n_pipe = max(0, min(n_full, n_tiles) - 1);
-  if (n_tiles > N / BC) n_pipe = max(0, min(n_pipe, N / BC - 2));
+  auto wait_all = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
 
-  // Tile j's K sits in K buffer j%2 and its V in V buffer j%2.  Step j (with
-  // the K stream one tile ahead): wait for K_{j+1}, V_j; start K_{j+2},
-  // V_{j+1}; compute.  On entry to step j the scores of tile j are in sa
-  // (masked) with the reference maximum, mc and alpha set for it.
+  // ---- the first item's operands ------------------------------------------------
+  // Tile j's K sits in K buffer j%2 and its V in V buffer j%2.  An item
+  // starts with its Q, K_0, K_1 and V_0 in flight; the previous item issued
+  // them at its last tile (V_0 only when V buffer 0 was free then).
+  int t_item = 0, bh, qb;
+  if (!item(0, bh, qb)) return;
+  __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + (size_t)bh * N * D, HEAD_BYTES);
+  __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + (size_t)bh * N * D, HEAD_BYTES);
+  int n_tiles = tiles_of(qb);
+  load_q(bh, qb);
+  load_kv(krs, koff, K0, 0);
+  load_kv(vrs, voff, V0, 0);
+  if (1 < n_tiles) load_kv(krs, koff, K1, 1);
+  bool v0_late = false;
   f32x16 sa[KB], sb[KB];
-  load_k(0);
-  load_v(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (1 < n_tiles) load_k(1);
-  w.scores(sa, 0);
-  if (needs_mask(0)) W::mask(sa, mask_lim(0));
-  w.max_all(sa);
 
-  auto top = [&](int j) {
-    // K_{j+1} and V_j have landed for this wave; the barrier makes every
-    // wave's loads visible and ends every wave's use of K_j and V_{j-1}
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 2 < n_tiles) load_k(j + 2);
-    if (j + 1 < n_tiles) load_v(j + 1);
-  };
-  auto top_full = [&](int j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 2 < n_tiles) load_tile<PER_W, ROW_BYTES, BC>(krs, kdst + (j & 1) * TILE_BYTES, koff, j + 2);
-    load_tile<PER_W, ROW_BYTES, BC>(vrs, vdst + ((j + 1) & 1) * TILE_BYTES, voff, j + 1);
-  };
-  // even tiles: K_{j+1} in buffer 1, V_j in buffer 0; odd tiles the other way
-  int j = 0;
-  for (; j + 1 < n_pipe; j += 2) {
-    top_full(j);
-    if (w.moved)
-      w.template pipe_tile<TILE_BYTES, 0, true>(sa, sb);
-    else
-      w.template pipe_tile<TILE_BYTES, 0, false>(sa, sb);
-    top_full(j + 1);
-    if (w.moved)
-      w.template pipe_tile<0, TILE_BYTES, true>(sb, sa);
-    else
-      w.template pipe_tile<0, TILE_BYTES, false>(sb, sa);
-  }
-  if (j < n_pipe) {
-    top_full(j);
-    w.template pipe_tile<TILE_BYTES, 0, true>(sa, sb);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
-    ++j;
-  }
+  for (;;) {
+    const int q0 = qb * BM;
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const int wr0 = q0 + wave * 32;              // first query row of this wave
+    const int qrow = wr0 + (lane & 31);          // this lane's query row
 
-  // ---- remaining tiles (diagonal, tail), masked where needed ---------------------
-  for (; j < n_tiles; ++j) {
-    top(j);
-    const int c0 = j * BC;
-    // a wave whose rows all precede a tile's first key has nothing to do
-    if (!CAUSAL || c0 <= wr0 + 31) w.finish(sa, (j & 1) * TILE_BYTES);
-    if (j + 1 < n_tiles && (!CAUSAL || c0 + BC <= wr0 + 31)) {
-      w.scores(sa, ((j + 1) & 1) * TILE_BYTES);
-      if (needs_mask(j + 1)) W::mask(sa, mask_lim(j + 1));
-      w.max_all(sa);
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      lane_offsets(ln, koff, voff);
+      read_offsets(ln);
     }
-  }
+    // the item's loads have landed, and every wave is done with the previous
+    // item's buffers
+    wait_all();
+    if (v0_late) load_kv(vrs, voff, V0, 0);
+    if (p.q_mode != 0) {
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk)   // negative scale: flip every sign; zero scale: zero
+        w.qf[kk] = p.q_mode == 1 ? (w.qf[kk] ^ 0x80008000u) : (u32x4){0, 0, 0, 0};
+    }
 
-  // ---- epilogue: O = acc / l, LSE = ln2 * (m*c + log2 l) -----------------
-  const float lt = pair_sum(w.l);
-  const float inv = 1.0f / lt;
-  if (qrow < N) {
-    float* orow = p.o + head_off + (size_t)qrow * D + 4 * (lane >> 5);
+    // ---- running state -------------------------------------------------------
+    w.m = -INFINITY;
+    w.l = 0.0f;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 val = {w.oacc[t][4 * r4 + 0] * inv, w.oacc[t][4 * r4 + 1] * inv,
-                           w.oacc[t][4 * r4 + 2] * inv, w.oacc[t][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + 32 * t + 8 * r4) = val;
+      for (int r = 0; r < 16; ++r) w.oacc[t][r] = 0.0f;
+
+    // mask limit of tile j for this lane (see Wave::mask), and whether any row
+    // of this wave needs the mask there
+    auto mask_lim = [&](int j) { return (CAUSAL ? min(qrow, N - 1) : N - 1) - j * BC - 4 * (lane >> 5); };
+    auto needs_mask = [&](int j) { return (CAUSAL && j * BC + BC - 1 > wr0) || j * BC + BC > N; };
+    // Tiles no row of the workgroup needs masked run software-pipelined: step j
+    // handles tile j and computes tile j+1's scores and maximum, so both must
+    // be such tiles; its loads (K_{j+2}, V_{j+1}) must not reach the tile that
+    // ends past N.  The rest run in a plain loop.
+    const int n_full = CAUSAL ? min(q0 / BC, N / BC) : N / BC;
+    int n_pipe = max(0, min(n_full, n_tiles) - 1);
+    if (n_tiles > N / BC) n_pipe = max(0, min(n_pipe, N / BC - 2));
+
+    // On entry to step j the scores of tile j are in sa (masked) with the
+    // reference maximum, mc and alpha set for it.  Step j (with the K stream
+    // one tile ahead): wait for K_{j+1}, V_j; start K_{j+2}, V_{j+1}; compute.
+    w.scores(sa, K0);
+    if (needs_mask(0)) W::mask(sa, mask_lim(0));
+    w.max_all(sa);
+
+    // Pipelined step j loads K_{j+2} (if any) into the K buffer tile j used and
+    // V_{j+1} into the other V buffer, both wholly inside the sequence, one
+    // 1 KiB piece at a time.  Even j: K_{j+1} is in K1, V_j in V0.
+    int j = 0;
+    auto ld_even = [&](int k) {
+      if (k < PER_W) {
+        if (j + 2 < n_tiles) load_one(krs, K0 + wofs + k * 1024, koff[k], (j + 2) * TILE_BYTES);
+      } else {
+        load_one(vrs, V1 + wofs + (k - PER_W) * 1024, voff[k - PER_W], (j + 1) * TILE_BYTES);
       }
-    if (lane < 32)
-      p.lse[(size_t)bh * N + qrow] = (w.m * w.c + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    };
+    auto ld_odd = [&](int k) {
+      if (k < PER_W) {
+        if (j + 2 < n_tiles) load_one(krs, K1 + wofs + k * 1024, koff[k], (j + 2) * TILE_BYTES);
+      } else {
+        load_one(vrs, V0 + wofs + (k - PER_W) * 1024, voff[k - PER_W], (j + 1) * TILE_BYTES);
+      }
+    };
+    constexpr int NL = 2 * PER_W;
+    for (; j + 1 < n_pipe; j += 2) {
+      wait_all();
+      if (w.moved)
+        w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
+      else
+        w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
+      ++j;
+      wait_all();
+      if (w.moved)
+        w.template pipe_tile<true, NL>(sb, sa, K0, V1, ld_odd);
+      else
+        w.template pipe_tile<false, NL>(sb, sa, K0, V1, ld_odd);
+      --j;
+    }
+    if (j < n_pipe) {
+      wait_all();
+      w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
+      ++j;
+    }
+
+    // ---- the remaining tiles: still pipelined with the next tile's scores,
+    // but the next tile may need its mask (causal diagonal, keys past N)
+    // before its maximum, and the loads may reach the tile that ends past N.
+    // The buffers alternate at run time here.
+    auto ld_any = [&](int k) {
+      const bool odd = j & 1;
+      if (k < PER_W) {
+        if (j + 2 < n_tiles)
+          load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, koff[k] + (j + 2 == j_tail ? tail_delta(k) : 0),
+                   (j + 2) * TILE_BYTES);
+      } else {
+        const int t = k - PER_W;
+        load_one(vrs, (odd ? V0 : V1) + wofs + t * 1024, voff[t] + (j + 1 == j_tail ? tail_delta(t) : 0),
+                 (j + 1) * TILE_BYTES);
+      }
+    };
+    for (; j + 1 < n_tiles; ++j) {
+      wait_all();
+      const bool odd = j & 1;
+      w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
+      if (needs_mask(j + 1)) W::mask(sb, mask_lim(j + 1));
+      w.max_all(sb);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
+    }
+
+    // ---- the last tile: P V only -----------------------------------------------------
+    wait_all();
+    // Both K buffers, and the V buffer the last tile does not use, are free
+    // now: start the next item's Q, K_0, K_1 and, when it is free, V_0.
+    int bh2 = 0, qb2 = 0;
+    const bool more = item(t_item + 1, bh2, qb2);
+    const __amdgpu_buffer_rsrc_t krs2 = head_rsrc(p.k + (size_t)bh2 * N * D, HEAD_BYTES);
+    const __amdgpu_buffer_rsrc_t vrs2 = head_rsrc(p.v + (size_t)bh2 * N * D, HEAD_BYTES);
+    const int n_tiles2 = tiles_of(qb2);
+    const bool last_odd = j & 1;
+    if (more) {
+      load_kv(krs2, koff, K0, 0);
+      if (1 < n_tiles2) load_kv(krs2, koff, K1, 1);
+      if (last_odd) load_kv(vrs2, voff, V0, 0);
+    }
+    // ---- epilogue: O = acc / l, LSE = ln2 * (m*c + log2 l) -----------------
+    // A lane holds 4-float pieces of one row of O, so storing from the
+    // accumulators writes 32 bytes into each of 32 rows per instruction.
+    // Instead each wave turns every 32x32 block of O row-major in a private
+    // 4 KiB of LDS (16-byte chunk c of row r at chunk c ^ ((r/2) % 8), so
+    // neither pattern has bank conflicts), and every store then writes 8
+    // whole 128-byte row pieces.
+    auto epilogue = [&](lds_u8* stage) {
+      const float lt = pair_sum(w.l);
+      const float inv = __builtin_amdgcn_rcpf(lt);
+      // lane-derived offsets computed here, not hoisted out of the item loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int h = ln >> 5, r = ln & 31;         // accumulator side: row r, chunks 2i + h
+      const int rs = ln >> 3, cs = ln & 7;        // store side: row 8s + rs, chunk cs
+      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+      // O of the head as a buffer: the rows past N-1 of a ragged last block
+      // fall outside it and their stores are dropped
+      const __amdgpu_buffer_rsrc_t ors = head_rsrc(p.o + head_off, (unsigned)N * D * 4);
+      const int vo = (wr0 + rs) * (D * 4) + cs * 16;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 val = {w.oacc[t][4 * i + 0] * inv, w.oacc[t][4 * i + 1] * inv,
+                             w.oacc[t][4 * i + 2] * inv, w.oacc[t][4 * i + 3] * inv};
+          *(lds_f32x4*)(stage + r * 128 + (((2 * i + h) ^ ((r >> 1) & 7)) << 4)) = val;
+        }
+#pragma unroll
+        for (int s8 = 0; s8 < 4; ++s8) {
+          const int row = 8 * s8 + rs;
+          const f32x4 val = *(const lds_f32x4*)(stage + row * 128 + ((cs ^ ((row >> 1) & 7)) << 4));
+          store_b128(ors, val, vo + s8 * 8 * D * 4 + t * 128);
+        }
+      }
+      if (qrow < N && lane < 32)
+        p.lse[(size_t)bh * N + qrow] = (w.m * w.c + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    };
+    // a wave whose rows all precede the tile's first key has nothing to do
+    if (!CAUSAL || j * BC <= wr0 + 31) w.finish(sa, last_odd ? V1 : V0);
+    if (more) load_q(bh2, qb2);   // the fragment registers are free from here on
+    if (D == 64) {
+      epilogue((lds_u8*)o_lds + wave * 4096);
+    } else {
+      __syncthreads();   // every wave is done reading the last tile's V buffer
+      epilogue((last_odd ? V1 : V0) + wave * 4096);
+    }
+    if (!more) break;
+    ++t_item;
+    bh = bh2;
+    qb = qb2;
+    krs = krs2;
+    vrs = vrs2;
+    n_tiles = n_tiles2;
+    v0_late = !last_odd;
   }
 }
 
 // ---- launch ------------------------------------------------------------------
 
 template <bool BF16, int D, bool CAUSAL>
-static hipError_t launch_one(const AttnParams& prm, int grid, hipStream_t stream) {
-  void* args[] = {const_cast<AttnParams*>(&prm)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL>),
-                         dim3(grid), dim3(kNW * 64), args, 0, stream);
+static const void* kernel_fn() {
+  return reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL>);
 }
 
 int block_rows(int d) {
@@ -627,22 +779,50 @@ int block_rows(int d) {
   return kBM;
 }
 
+// Workgroups of one kernel variant that the current device runs at once
+// (compute units x workgroups per compute unit), cached per device.
+static int resident_groups(int variant, const void* fn) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[8][kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cache[variant][dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kNW * 64, 0) != hipSuccess) return -1;
+  const int n = std::max(1, cus) * std::max(1, per_cu);
+  if (dev >= 0 && dev < kMaxDev) cache[variant][dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, hipStream_t stream) {
   const int bm = block_rows(d);
   prm.n_qblk = (prm.N + bm - 1) / bm;
-  prm.xcd_remap = (prm.BH % 8 == 0) ? 1 : 0;
   // raw-score margin before the reference maximum moves: 0 for bf16 (exact
   // running maximum), 2^8 in probability units for fp16
   prm.thr = bf16 ? 0.0f : fminf(8.0f / prm.c, 3.0e38f);
-  const long long grid = (long long)prm.BH * prm.n_qblk;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int g = (int)grid;
-  if (bf16) {
-    if (d == 64) return causal ? launch_one<true, 64, true>(prm, g, stream) : launch_one<true, 64, false>(prm, g, stream);
-    return causal ? launch_one<true, 128, true>(prm, g, stream) : launch_one<true, 128, false>(prm, g, stream);
-  }
-  if (d == 64) return causal ? launch_one<false, 64, true>(prm, g, stream) : launch_one<false, 64, false>(prm, g, stream);
-  return causal ? launch_one<false, 128, true>(prm, g, stream) : launch_one<false, 128, false>(prm, g, stream);
+  const long long items = (long long)prm.BH * prm.n_qblk;
+  if (items > (1LL << 30)) return hipErrorInvalidConfiguration;
+
+  const int variant = (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
+  const void* fn = bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true>() : kernel_fn<true, 64, false>())
+                                   : (causal ? kernel_fn<true, 128, true>() : kernel_fn<true, 128, false>()))
+                        : (d == 64 ? (causal ? kernel_fn<false, 64, true>() : kernel_fn<false, 64, false>())
+                                   : (causal ? kernel_fn<false, 128, true>() : kernel_fn<false, 128, false>()));
+  const int slots = resident_groups(variant, fn);
+  if (slots < 0) return hipErrorInvalidDevice;
+  // heads split over the 8 XCDs when they divide evenly
+  prm.n_dom = (prm.BH % 8 == 0) ? 8 : 1;
+  const long long per_dom = items / prm.n_dom;
+  prm.n_work = (int)std::min<long long>(std::max(1, slots / prm.n_dom), per_dom);
+  prm.grp = std::max(1, prm.n_work / prm.n_qblk);
+  const int grid = prm.n_dom * prm.n_work;
+
+  void* args[] = {&prm};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kNW * 64), args, 0, stream);
 }
 
 }  // namespace ttc

@@ -14,7 +14,9 @@ struct AttnParams {
   int BH;              // batch * heads
   int N;               // sequence length
   int n_qblk;          // query blocks per head (set by the launcher)
-  int xcd_remap;       // 1: keep each head's blocks on one XCD (set by the launcher)
+  int n_dom;           // head domains, one per XCD (8) or a single one (1) (set by the launcher)
+  int n_work;          // workgroups per domain (set by the launcher)
+  int grp;             // heads per group in a domain's item order (set by the launcher)
   float c;             // |scale| * log2(e), or log2(e) when scale == 0
   float thr;           // raw-score margin before the running maximum moves (set by the launcher)
   int q_mode;          // 0: use Q; 1: use -Q (negative scale); 2: use 0 (zero scale)
