@@ -238,6 +238,32 @@ struct Wave {
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
   }
+  // The causal mask of a tile that starts delta = c0 - wr0 keys after the
+  // wave's first query row (a multiple of 32 for these tile shapes), for a
+  // tile wholly inside the sequence.  delta >= 32: every key follows every
+  // row; delta = 0: block 0 is the triangle, block 1 all future keys;
+  // delta = -32: block 1 is the triangle.  In the triangle, key
+  // 8*(r/4) + r%4 + 4*(lane/32) of the block is hidden from row lane%32 when
+  // it is larger; the lanes that hide score r form a constant mask.  Each
+  // score takes one v_cndmask on a mask the scalar unit selects.
+  TTC_INLINE static constexpr unsigned long long tri_lanes(int r) {
+    unsigned long long m = 0;
+    for (int l = 0; l < 64; ++l)
+      if (8 * (r >> 2) + (r & 3) + 4 * (l >> 5) > (l & 31)) m |= 1ull << l;
+    return m;
+  }
+  TTC_INLINE static void diag_mask(f32x16 (&s)[KB], int delta) {
+    static_assert(KB == 2, "two 32-key blocks per tile");
+    const bool all = delta >= 32, zero = delta == 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned long long t = tri_lanes(r);
+      const unsigned long long m0 = all ? ~0ull : (zero ? t : 0ull);
+      const unsigned long long m1 = (all || zero) ? ~0ull : t;
+      s[0][r] = __builtin_amdgcn_inverse_ballot_w64(m0) ? -INFINITY : s[0][r];
+      s[1][r] = __builtin_amdgcn_inverse_ballot_w64(m1) ? -INFINITY : s[1][r];
+    }
+  }
   // The row's tile maximum mx (both lane halves) moves the reference
   // maximum if some row of the wave outgrew it by the margin (always on the
   // first tile, where m is -inf); sets alpha and mc for the tile.
@@ -415,8 +441,11 @@ TTC_INLINE __amdgpu_buffer_rsrc_t head_rsrc(const void* base, unsigned nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 
+// Stores of O are marked non-temporal (cache policy bit 1, "nt" on gfx950):
+// O is written once, and keeping it out of L2 leaves room for the K/V tiles
+// the other query blocks of a head still read.
 TTC_INLINE void store_b128(__amdgpu_buffer_rsrc_t rs, f32x4 v, int voff) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 2);
 }
 
 template <bool BF16, int D, bool CAUSAL>
@@ -491,7 +520,7 @@ attn_fwd_kernel(AttnParams p) {
     const int row = min(qb * BM + wave * 32 + (lane & 31), N - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(p.q + (size_t)bh * N * D + (size_t)row * D + 8 * (lane >> 5));
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) w.qf[kk] = src[2 * kk];
+    for (int kk = 0; kk < DK; ++kk) w.qf[kk] = __builtin_nontemporal_load(src + 2 * kk);   // read once
   };
 
   // ---- K/V tile loads: HBM -> LDS directly ----------------------------------
@@ -566,6 +595,31 @@ attn_fwd_kernel(AttnParams p) {
   // Tile j's K sits in K buffer j%2 and its V in V buffer j%2.  An item
   // starts with its Q, K_0, K_1 and V_0 in flight; the previous item issued
   // them at its last tile (V_0 only when V buffer 0 was free then).
+  // Of the two workgroups on a CU the older one wins issue arbitration, and
+  // with equal lists it would finish well before the younger one.  Each
+  // workgroup therefore lowers its priority as it gets through its list
+  // (3 for the first half of its tiles, 2 to three quarters, 1 to nine
+  // tenths, then 0): whichever of the two is behind wins, and they finish
+  // together.
+  int tot_tiles = 0;
+  for (int t = 0;; ++t) {
+    int b2, q2;
+    if (!item(t, b2, q2)) break;
+    tot_tiles += tiles_of(q2);
+  }
+  const int th1 = tot_tiles / 2, th2 = (3 * tot_tiles) / 4, th3 = (9 * tot_tiles) / 10;
+  int done_tiles = 0;
+  auto progress = [&]() {
+    ++done_tiles;
+    if (done_tiles < th1)
+      __builtin_amdgcn_s_setprio(3);
+    else if (done_tiles < th2)
+      __builtin_amdgcn_s_setprio(2);
+    else if (done_tiles < th3)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
   int t_item = 0, bh, qb;
   if (!item(0, bh, qb)) return;
   __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + (size_t)bh * N * D, HEAD_BYTES);
@@ -612,6 +666,13 @@ attn_fwd_kernel(AttnParams p) {
     // of this wave needs the mask there
     auto mask_lim = [&](int j) { return (CAUSAL ? min(qrow, N - 1) : N - 1) - j * BC - 4 * (lane >> 5); };
     auto needs_mask = [&](int j) { return (CAUSAL && j * BC + BC - 1 > wr0) || j * BC + BC > N; };
+    auto apply_mask = [&](f32x16 (&s)[KB], int j) {
+      if (!needs_mask(j)) return;
+      if (CAUSAL && j * BC + BC <= N)
+        W::diag_mask(s, j * BC - wr0);
+      else
+        W::mask(s, mask_lim(j));
+    };
     // Tiles no row of the workgroup needs masked run software-pipelined: step j
     // handles tile j and computes tile j+1's scores and maximum, so both must
     // be such tiles; its loads (K_{j+2}, V_{j+1}) must not reach the tile that
@@ -624,7 +685,7 @@ attn_fwd_kernel(AttnParams p) {
     // reference maximum, mc and alpha set for it.  Step j (with the K stream
     // one tile ahead): wait for K_{j+1}, V_j; start K_{j+2}, V_{j+1}; compute.
     w.scores(sa, K0);
-    if (needs_mask(0)) W::mask(sa, mask_lim(0));
+    apply_mask(sa, 0);
     w.max_all(sa);
 
     // Pipelined step j loads K_{j+2} (if any) into the K buffer tile j used and
@@ -648,12 +709,14 @@ attn_fwd_kernel(AttnParams p) {
     constexpr int NL = 2 * PER_W;
     for (; j + 1 < n_pipe; j += 2) {
       wait_all();
+      progress();
       if (w.moved)
         w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
       else
         w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
       ++j;
       wait_all();
+      progress();
       if (w.moved)
         w.template pipe_tile<true, NL>(sb, sa, K0, V1, ld_odd);
       else
@@ -662,6 +725,7 @@ attn_fwd_kernel(AttnParams p) {
     }
     if (j < n_pipe) {
       wait_all();
+      progress();
       w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
@@ -686,13 +750,17 @@ attn_fwd_kernel(AttnParams p) {
     };
     for (; j + 1 < n_tiles; ++j) {
       wait_all();
+      progress();
+      // causal: the next tile may be the last and wholly after this wave's
+      // rows (then it is the item's last tile)
       const bool odd = j & 1;
       w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
-      if (needs_mask(j + 1)) W::mask(sb, mask_lim(j + 1));
+      apply_mask(sb, j + 1);
       w.max_all(sb);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
     }
+
 
     // ---- the last tile: P V only -----------------------------------------------------
     wait_all();
