@@ -164,6 +164,12 @@ TTC_INLINE float pair_sum(float x) {
 
 TTC_INLINE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of three, NaN-propagating (v_maximum3_f32 on gfx950: no operand
+// canonicalisation, unlike fmaxf in IEEE mode).
+TTC_INLINE float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 constexpr int kBC = 64;        // keys per K/V tile
 constexpr int kNW = 4;         // waves per workgroup
 constexpr int kBM = kNW * 32;  // query rows per workgroup
@@ -281,7 +287,7 @@ struct Wave {
   TTC_INLINE void max_all(f32x16 (&s)[KB]) {
     float mx = s[0][0];
 #pragma unroll
-    for (int v = 1; v < NS; ++v) mx = fmaxf(mx, at(s, v));
+    for (int v = 1; v < NS; ++v) mx = __builtin_elementwise_maximum(mx, at(s, v));
     new_max(mx);
   }
   TTC_INLINE void prob(f32x16 (&s)[KB], int v) { s[v >> 4][v & 15] = fast_exp2(__builtin_fmaf(at(s, v), c, -mc)); }
@@ -345,7 +351,7 @@ struct Wave {
 #pragma unroll
     for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
     float rs[NS / 2];
-    float mp[11], q[4];
+    float mp[10], q[4];
 #pragma unroll
     for (int g = 0; g < NSTEP; ++g) {
       const bool p1 = g < NQK;
@@ -390,28 +396,25 @@ struct Wave {
             for (int k = 0; k < 4; ++k) rs[k] = rs[2 * k] + rs[2 * k + 1];
             if (MAXN) {
 #pragma unroll
-              for (int k = 0; k < 4; ++k)
-                mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+              for (int k = 0; k < 4; ++k) mp[k] = max3(at(sn, 3 * k), at(sn, 3 * k + 1), at(sn, 3 * k + 2));
             }
           } else if (cc == 13) {
             rs[0] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
             l = RESCALE ? __builtin_fmaf(l, alpha, rs[0]) : l + rs[0];
             if (MAXN) {
 #pragma unroll
-              for (int k = 4; k < 8; ++k)
-                mp[k] = fmaxf(fmaxf(at(sn, 3 * k), at(sn, 3 * k + 1)), at(sn, 3 * k + 2));
+              for (int k = 4; k < 8; ++k) mp[k] = max3(at(sn, 3 * k), at(sn, 3 * k + 1), at(sn, 3 * k + 2));
             }
           } else if (!MAXN) {
           } else if (cc == 14) {
-            mp[8] = fmaxf(fmaxf(at(sn, 24), at(sn, 25)), at(sn, 26));
-            mp[9] = fmaxf(fmaxf(at(sn, 27), at(sn, 28)), at(sn, 29));
-            mp[10] = fmaxf(at(sn, 30), at(sn, 31));
-            q[0] = fmaxf(fmaxf(mp[0], mp[1]), mp[2]);
-            q[1] = fmaxf(fmaxf(mp[3], mp[4]), mp[5]);
-            q[2] = fmaxf(fmaxf(mp[6], mp[7]), mp[8]);
-            q[3] = fmaxf(mp[9], mp[10]);
+            mp[8] = max3(at(sn, 24), at(sn, 25), at(sn, 26));
+            mp[9] = max3(at(sn, 27), at(sn, 28), at(sn, 29));
+            q[0] = max3(mp[0], mp[1], mp[2]);
+            q[1] = max3(mp[3], mp[4], mp[5]);
+            q[2] = max3(mp[6], mp[7], mp[8]);
+            q[3] = max3(mp[9], at(sn, 30), at(sn, 31));
           } else {
-            new_max(fmaxf(fmaxf(fmaxf(q[0], q[1]), q[2]), q[3]));
+            new_max(max3(q[0], q[1], __builtin_elementwise_maximum(q[2], q[3])));
           }
         }
       }
@@ -821,8 +824,16 @@ attn_fwd_kernel(AttnParams p) {
     if (D == 64) {
       epilogue((lds_u8*)o_lds + wave * 4096);
     } else {
-      __syncthreads();   // every wave is done reading the last tile's V buffer
-      epilogue((last_odd ? V1 : V0) + wave * 4096);
+      // V buffer 1 takes the staging: when the last tile is even it held
+      // tile j-1 and is free since the last tile's barrier; when it is odd
+      // the other waves may still be reading it, so wait for them (a plain
+      // barrier: __syncthreads() would also wait for the next item's loads,
+      // none of which writes V buffer 1).
+      if (last_odd) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+      }
+      epilogue(V1 + wave * 4096);
     }
     if (!more) break;
     ++t_item;
