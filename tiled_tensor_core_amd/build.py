@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import argparse
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -29,6 +30,12 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels' per-tile step loops are unrolled in full by pragma; the
+    # default size limit would leave the largest one rolled, and its
+    # register arrays in scratch memory
+    "-mllvm", "-pragma-unroll-threshold=1000000",
+    # per-kernel resource report, checked below for scratch use
+    "-Rpass-analysis=kernel-resource-usage",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
@@ -54,9 +61,21 @@ def build(isa_dir: str | None = None, verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
+    lines = [line for line in res.stderr.splitlines() if noise not in line]
+    report = [line for line in lines if "kernel-resource-usage" in line]
+    err = "\n".join(line for line in lines if "kernel-resource-usage" not in line)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    # every kernel is designed to live in registers: scratch means spills or
+    # a register array the compiler could not keep in registers
+    kernel = None
+    for line in report:
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            print(f"warning: {kernel} uses {m.group(1)} bytes of scratch per lane", file=sys.stderr)
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB_PATH)

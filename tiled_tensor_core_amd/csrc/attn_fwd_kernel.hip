@@ -147,6 +147,21 @@ struct Swz<64> {
   TTC_INLINE static int v(int r) { return 4 * ((r >> 1) & 1); }
 };
 
+// Causal triangle of a 32x32 score block in the transposed accumulator
+// layout: bit l of m[r] is set when lane l's score r (key 8*(r/4) + r%4 +
+// 4*(l/32) of the block) follows the lane's query row (l % 32).
+struct TriLanes {
+  unsigned long long m[16];
+};
+constexpr TriLanes make_tri_lanes() {
+  TriLanes t{};
+  for (int r = 0; r < 16; ++r)
+    for (int l = 0; l < 64; ++l)
+      if (8 * (r >> 2) + (r & 3) + 4 * (l >> 5) > (l & 31)) t.m[r] |= 1ull << l;
+  return t;
+}
+constexpr TriLanes kTriLanes = make_tri_lanes();
+
 // Row reductions across the two lane halves: lanes l and l ^ 32 hold the
 // two halves of one query row.  v_permlane32_swap(x, x) gives lanes 0-31
 // (own, lane + 32) and lanes 32-63 (lane - 32, own), so combining the two
@@ -252,23 +267,21 @@ struct Wave {
   // 8*(r/4) + r%4 + 4*(lane/32) of the block is hidden from row lane%32 when
   // it is larger; the lanes that hide score r form a constant mask.  Each
   // score takes one v_cndmask on a mask the scalar unit selects.
-  TTC_INLINE static constexpr unsigned long long tri_lanes(int r) {
-    unsigned long long m = 0;
-    for (int l = 0; l < 64; ++l)
-      if (8 * (r >> 2) + (r & 3) + 4 * (l >> 5) > (l & 31)) m |= 1ull << l;
-    return m;
+  TTC_INLINE static unsigned long long tri_lanes(int r) { return kTriLanes.m[r]; }
+  // Lanes that hide score r of 32-key block kb, whose first key is db =
+  // delta + 32*kb keys after the wave's first row: all (db >= 32), the
+  // triangle (db = 0) or none (db <= -32).
+  TTC_INLINE static unsigned long long diag_lanes(int delta, int kb, int r) {
+    const int db = delta + 32 * kb;
+    return db >= 32 ? ~0ull : (db == 0 ? tri_lanes(r) : 0ull);
+  }
+  TTC_INLINE static void diag_mask_one(f32x16 (&s)[KB], int delta, int e) {   // score e = 16*kb + r
+    const int kb = e >> 4, r = e & 15;
+    s[kb][r] = __builtin_amdgcn_inverse_ballot_w64(diag_lanes(delta, kb, r)) ? -INFINITY : s[kb][r];
   }
   TTC_INLINE static void diag_mask(f32x16 (&s)[KB], int delta) {
-    static_assert(KB == 2, "two 32-key blocks per tile");
-    const bool all = delta >= 32, zero = delta == 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const unsigned long long t = tri_lanes(r);
-      const unsigned long long m0 = all ? ~0ull : (zero ? t : 0ull);
-      const unsigned long long m1 = (all || zero) ? ~0ull : t;
-      s[0][r] = __builtin_amdgcn_inverse_ballot_w64(m0) ? -INFINITY : s[0][r];
-      s[1][r] = __builtin_amdgcn_inverse_ballot_w64(m1) ? -INFINITY : s[1][r];
-    }
+    for (int e = 0; e < NS; ++e) diag_mask_one(s, delta, e);
   }
   // The row's tile maximum mx (both lane halves) moves the reference
   // maximum if some row of the wave outgrew it by the margin (always on the
@@ -343,9 +356,12 @@ struct Wave {
   // writes do not all land with the tile's first reads.
   // MAXN = false leaves tile j+1's maximum (and m, mc, alpha) to the caller,
   // for a next tile that must be masked first.
-  template <bool RESCALE, int NLOAD, class LD, bool MAXN = true>
+  // MASKN: tile j+1 is a causal diagonal tile starting mdelta keys after
+  // the wave's first row; its mask goes in during slices 8-11 of phase 2,
+  // ahead of the maximum.
+  template <bool RESCALE, int NLOAD, class LD, bool MAXN = true, bool MASKN = false>
   TTC_INLINE void pipe_tile(f32x16 (&s)[KB], f32x16 (&sn)[KB], const lds_u8* kt, const lds_u8* vt,
-                            const LD& ld) {
+                            const LD& ld, int mdelta = 0) {
     constexpr int L = kLead, NSTEP = NQK + NPV;
     u32x4 op[L];
 #pragma unroll
@@ -380,6 +396,10 @@ struct Wave {
           }
         } else {
           const int t = cc / 4 + 1;
+          if (MASKN && cc >= 8 && cc < 12) {
+#pragma unroll
+            for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
+          }
           if (RESCALE && t < DT) {
 #pragma unroll
             for (int r = 4 * (cc % 4); r < 4 * (cc % 4) + 4; ++r) oacc[t][r] *= alpha;
@@ -671,7 +691,7 @@ attn_fwd_kernel(AttnParams p) {
     auto needs_mask = [&](int j) { return (CAUSAL && j * BC + BC - 1 > wr0) || j * BC + BC > N; };
     auto apply_mask = [&](f32x16 (&s)[KB], int j) {
       if (!needs_mask(j)) return;
-      if (CAUSAL && j * BC + BC <= N)
+      if (CAUSAL)   // keys past N follow every row below N
         W::diag_mask(s, j * BC - wr0);
       else
         W::mask(s, mask_lim(j));
@@ -757,9 +777,16 @@ attn_fwd_kernel(AttnParams p) {
       // causal: the next tile may be the last and wholly after this wave's
       // rows (then it is the item's last tile)
       const bool odd = j & 1;
-      w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
-      apply_mask(sb, j + 1);
-      w.max_all(sb);
+      if constexpr (CAUSAL) {
+        // a causal diagonal tile, masked in the pipeline (keys past N follow
+        // every row below N, so the causal mask hides them as well)
+        w.template pipe_tile<true, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
+                                                                     (j + 1) * BC - wr0);
+      } else {
+        w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
+        apply_mask(sb, j + 1);
+        w.max_all(sb);
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
     }
