@@ -8,9 +8,20 @@ JSON line with whole-job TFLOP/s, the MFMA roofline fraction of the kernel
 on a bounded sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload llama] [--no-cpu-baseline]
+    python bench.py --kernel softmax [--softmax-workload scores]
 
 FLOPs are algorithmic: 4*B*H*N^2*d, halved when causal (masked-tile waste and
 padding are not counted).
+
+Warm-up runs W untimed steps and continues until at least 0.5 s of GPU work
+has passed: the GPU reaches its sustained clocks only after tens of
+milliseconds of load, and timing before that under-reports a loaded GPU by
+about 10 %.
+
+``--kernel softmax`` times the row-wise softmax entry point ``softmax_rows``
+instead: a step is one softmax over a [rows, cols] matrix resident in HBM,
+reported in GB/s of algorithmic traffic (each element read once and written
+once) against the HBM roofline.
 """
 
 from __future__ import annotations
@@ -34,6 +45,8 @@ PEAK_TFLOPS = 2516.6          # MI355X dense bf16/fp16 MFMA
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "attn_fwd_kernel.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b8h32n2048d128_traffic.txt")
+SOFTMAX_METRIC = "row softmax GB/s (algorithmic bytes: one read and one write per element) + % of MI355X HBM peak"
+SOFTMAX_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "softmax_kernel.hip")
 
 
 def flops(B, H, N, d, causal):
@@ -41,54 +54,84 @@ def flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path=KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    if not h or not t or h.group(1) != kernel_source_hash(src):
         return None
     return float(t.group(1))
 
 
-def time_workload(attn, torch, w, causal, steps, warmup, inputs):
-    q, k, v = inputs
-    B, H, N, d = w.B, w.H, w.N, w.d
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream)
+WARMUP_MIN_S = 0.5
+
+
+def warm_up(torch, launch, warmup, min_seconds=WARMUP_MIN_S):
+    """Run ``warmup`` untimed launches, and more until ``min_seconds`` of
+    wall time have passed with the GPU busy (synchronising every 8 launches,
+    so the clock follows the GPU).  The GPU raises its clocks only after tens
+    of milliseconds of sustained load: a timed loop that starts after a few
+    milliseconds of warm-up runs about 10 % slower than every later one."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_seconds:
+        launch()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    return n
+
+
+def time_launches(torch, launch, stream, steps, warmup, warmup_s=WARMUP_MIN_S):
+    """Time ``steps`` calls of ``launch()`` on ``stream`` after the warm-up.
+    The whole-loop time per step comes from a loop bracketed by two events
+    only; the per-launch times from a second loop of the same length with an
+    event pair around each launch."""
+    warm_up(torch, launch, warmup, warmup_s)
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_all0.record(stream)
-    for i in range(steps):
-        starts[i].record(stream)
-        attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream)
-        ends[i].record(stream)
+    for _ in range(steps):
+        launch()
     t_all1.record(stream)
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(st.elapsed_time(e) for st, e in zip(starts, ends))
     return {
         "ms_per_step": total_ms / steps,
         "kernel_ms_mean": float(np.mean(per)),
         "kernel_ms_median": float(np.median(per)),
         "kernel_ms_min": float(per[0]),
-        "flops": flops(B, H, N, d, causal),
     }
+
+
+def time_workload(attn, torch, w, causal, steps, warmup, inputs, warmup_s=WARMUP_MIN_S):
+    q, k, v = inputs
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    r = time_launches(torch, lambda: attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream),
+                      stream, steps, warmup, warmup_s)
+    r["flops"] = flops(B, H, N, d, causal)
+    return r
 
 
 def cpu_baseline(w, causal, bits, budget_s):
@@ -130,13 +173,116 @@ def cpu_baseline(w, causal, bits, budget_s):
     }
 
 
+def softmax_cpu_baseline(w, x, budget_s):
+    """The fp64 softmax oracle on blocks of rows of the workload until
+    ``budget_s`` of CPU time has passed (or every row is done); GB/s over the
+    same algorithmic bytes.  numpy's element-wise max, exp and sum run on one
+    thread, so one core is used."""
+    from oracle import softmax_rows_ref
+    from tiled_tensor_core_amd import synth
+
+    block = max(1, (1 << 21) // w.cols)      # about 2M elements per call
+    done = 0
+    elapsed = 0.0
+    t0 = time.perf_counter()
+    for r0 in range(0, w.rows, block):
+        xb = synth.softmax_to_f64(x[r0:r0 + block], w.dtype)
+        ts = time.perf_counter()
+        softmax_rows_ref(xb)
+        elapsed += time.perf_counter() - ts
+        done += xb.shape[0]
+        if elapsed >= budget_s:
+            break
+    nbytes = 2.0 * done * w.cols * w.elem_bytes
+    return {
+        "value": nbytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {w.rows} rows (all {w.cols} columns each), fp64 numpy, "
+                  f"{elapsed:.1f} s; wall {time.perf_counter() - t0:.1f} s",
+    }
+
+
+def run_softmax(a, torch, attn, synth):
+    w = synth.SOFTMAX_WORKLOADS[a.softmax_workload]
+    print(f"[bench] generating softmax input {w.describe()}", file=sys.stderr, flush=True)
+    x = synth.make_softmax_workload(w)
+    xt = synth.softmax_to_torch(x, w.dtype, "cuda")
+    yt = torch.empty_like(xt)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} softmax steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
+    r = time_launches(torch, lambda: attn.softmax_rows(xt, yt, w.rows, w.cols, stream=stream),
+                      stream, a.steps, a.warmup, a.warmup_seconds)
+    nbytes = 2.0 * w.rows * w.cols * w.elem_bytes
+    value = nbytes / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (r["kernel_ms_mean"] * 1e-3) / 1e9
+    traffic = measured_traffic(os.path.join(ROOT, "profiles", f"softmax_{w.name}_r{w.rows}c{w.cols}_traffic.txt"),
+                               SOFTMAX_SRC)
+    out = {
+        "metric": SOFTMAX_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"row softmax {w.name} {w.describe()}", "rows": w.rows, "cols": w.cols,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+            "kernel_ms_median": round(r["kernel_ms_median"], 5),
+        },
+    }
+    if a.extra:
+        per = {}
+        for name, ow in synth.SOFTMAX_WORKLOADS.items():
+            ox = synth.softmax_to_torch(synth.make_softmax_workload(ow), ow.dtype, "cuda")
+            oy = torch.empty_like(ox)
+            rr = time_launches(torch, lambda: attn.softmax_rows(ox, oy, ow.rows, ow.cols, stream=stream),
+                               stream, 20, 5, a.warmup_seconds)
+            per[f"{name} {ow.describe()}"] = round(
+                2.0 * ow.rows * ow.cols * ow.elem_bytes / (rr["kernel_ms_median"] * 1e-3) / 1e9, 1)
+            del ox, oy
+            print(f"[bench] timed softmax {name}", file=sys.stderr, flush=True)
+        out["per_workload_gbs"] = per
+        # a plain device-to-device copy of the same bytes (torch's copy kernel),
+        # as an empirical ceiling for a read-once, write-once kernel
+        rc = time_launches(torch, lambda: yt.copy_(xt), stream, 20, 5, a.warmup_seconds)
+        out["copy_same_bytes_gbs"] = round(nbytes / (rc["kernel_ms_median"] * 1e-3) / 1e9, 1)
+    if not a.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{a.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = softmax_cpu_baseline(w, x, a.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama")
+    ap.add_argument("--kernel", choices=["attention", "softmax"], default="attention",
+                    help="which entry point to time (default: the attention forward pass)")
+    ap.add_argument("--softmax-workload", default="scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warmup-seconds", type=float, default=WARMUP_MIN_S,
+                    help="minimum warm-up time in seconds (0: exactly --warmup steps, as counter runs want)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (causal and non-causal) and report them")
@@ -170,6 +316,9 @@ def main():
         print(f"[bench] copied {n * 4} bytes three times", file=sys.stderr, flush=True)
         del src, dst
         torch.cuda.empty_cache()
+    if a.kernel == "softmax":
+        run_softmax(a, torch, attn, synth)
+        return
     w = synth.WORKLOADS[a.workload]
     causal = w.causal[-1]
     print(f"[bench] generating {w.name} inputs {w.describe()}", file=sys.stderr, flush=True)
@@ -177,7 +326,7 @@ def main():
     inputs = tuple(synth.to_torch(x, w.dtype, "cuda") for x in bits)
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
-    r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs)
+    r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs, a.warmup_seconds)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     # the committed counter summary covers the causal B=8 H=32 N=2048 d=128 run
@@ -218,7 +367,7 @@ def main():
             ob = bits if name == w.name else synth.make_workload(ow)
             oin = inputs if name == w.name else tuple(synth.to_torch(x, ow.dtype, "cuda") for x in ob)
             for c in (False, True):
-                rr = time_workload(attn, torch, ow, c, 20, 5, oin)
+                rr = time_workload(attn, torch, ow, c, 20, 5, oin, a.warmup_seconds)
                 per[f"{name} {'causal' if c else 'non-causal'}"] = round(
                     rr["flops"] / (rr["kernel_ms_median"] * 1e-3) / 1e12, 2)
             del oin

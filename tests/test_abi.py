@@ -13,6 +13,7 @@ from tiled_tensor_core_amd import attn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "softmax.h")]
 
 # fake, 16-byte-aligned, well separated "device" addresses: validation never
 # dereferences them, and every case below fails validation
@@ -32,9 +33,12 @@ def _call(fn="attn_fwd", dtype=0, **over):
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = open(header).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b((?:attn|softmax)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_names():
@@ -47,7 +51,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (attn_[a-z0-9_]+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT ((?:attn|softmax)_[a-z0-9_]+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -115,3 +119,22 @@ def test_missing_library_fails_loudly(tmp_path):
             mod.load_library(str(tmp_path / "nope.so"))
     finally:
         importlib.reload(attn)
+
+
+# ---- row softmax entry point -------------------------------------------------
+
+SM_GOOD = dict(x=Q, y=O, rows=4, cols=100, dtype=1)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=0), 1), (dict(y=0), 1),
+    (dict(rows=0), 2), (dict(cols=0), 2), (dict(rows=-1), 2), (dict(cols=1 << 30), 2),
+    (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(x=Q + 2), 4), (dict(y=O + 8), 4),
+    (dict(y=Q + 16), 9),
+])
+def test_softmax_rejects_invalid_arguments(over, code):
+    a = dict(SM_GOOD)
+    a.update(over)
+    lib = attn.load_library()
+    assert lib.softmax_rows(a["x"], a["y"], a["rows"], a["cols"], a["dtype"], None) == code

@@ -1,0 +1,138 @@
+"""GPU parity of the row-wise softmax kernel (C ABI ``softmax_rows``) against
+the fp64 oracle (oracle/softmax.py) on seeded inputs.
+
+Tolerance: the kernel computes in fp32 and rounds the output to the input
+type, so an entry may differ from the exact value by the output's rounding
+plus a few fp32 ulps of the exponent: |y - y_ref| <= rel * |y_ref| + abs with
+rel = 2^-8 (bf16, half an ulp is 2^-9), 2^-10 (fp16, 2^-11) and 5e-5 (fp32,
+exponent arguments up to ~400 carry ~1e-5 of fp32 rounding); abs covers
+the smallest outputs: the hardware base-2 exponential flushes results below
+2^-126 to zero (fp32 and bf16 share that exponent range), and fp16 outputs
+below 2^-14 are subnormal with a spacing of 2^-24.  Row sums must be 1 within
+rel plus abs times the row length.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import softmax_rows_ref
+from tiled_tensor_core_amd import synth
+from parity import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+TOL = {"fp32": (5e-5, 2.0 ** -126), "bf16": (2.0 ** -8, 2.0 ** -126), "fp16": (2.0 ** -10, 2.0 ** -24)}
+
+
+def _to_f64(t, dtype):
+    import torch
+
+    if dtype == "fp32":
+        return t.cpu().numpy().astype(np.float64)
+    bits = t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return synth.bits_to_f64(bits, dtype)
+
+
+def run_gpu(x, dtype, inplace=False):
+    """Run the kernel on input x (host array); returns the output as float64."""
+    from tiled_tensor_core_amd import attn
+
+    xt = synth.softmax_to_torch(x, dtype, "cuda")
+    if inplace:
+        attn.softmax_rows(xt, xt, xt.shape[0], xt.shape[1])
+        yt = xt
+    else:
+        yt = attn.softmax(xt)
+    import torch
+
+    torch.cuda.synchronize()
+    return _to_f64(yt, dtype)
+
+
+def check(y, ref, dtype, tag):
+    rel, ab = TOL[dtype]
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(y), np.isnan(ref)), f"{tag}: NaN pattern differs"
+    err = np.abs(y[fin] - ref[fin])
+    bound = rel * np.abs(ref[fin]) + ab
+    worst = float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
+    print(f"[softmax parity] {tag}: max err/bound {worst:.3f}, max abs err {float(err.max()) if err.size else 0:.3e}",
+          flush=True)
+    assert np.all(err <= bound), f"{tag}: worst err/bound {worst}"
+    rows_ok = np.all(np.isfinite(ref), axis=1)
+    if np.any(rows_ok):
+        sums = y[rows_ok].sum(axis=1)
+        assert np.all(np.abs(sums - 1.0) <= rel * 1.0 + ab * y.shape[1] + 1e-6), f"{tag}: row sums {sums}"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("rows,cols", [
+    (1, 1), (3, 7), (5, 8), (2, 4), (64, 512), (33, 1000), (17, 2048), (9, 4096), (7, 8192),
+    (3, 8200), (4, 12345), (2, 40000), (2, 65536), (2, 65544), (3, 70000), (1, 300000),
+])
+def test_shapes(dtype, rows, cols):
+    x = synth.make_softmax_input(rows, cols, dtype, seed=rows * 7919 + cols)
+    y = run_gpu(x, dtype)
+    check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"{dtype} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_in_place(dtype):
+    x = synth.make_softmax_input(10, 3000, dtype, seed=5)
+    y = run_gpu(x, dtype, inplace=True)
+    check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"in place {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("cols", [64, 1000, 20000, 70000])
+def test_minus_inf_and_nan_rows(dtype, cols):
+    """-inf entries weigh 0; an all -inf row and a row holding NaN come out NaN."""
+    x = synth.softmax_to_f64(synth.make_softmax_input(6, cols, dtype, seed=cols), dtype).astype(np.float32)
+    x[0, ::3] = -np.inf
+    x[1, :] = -np.inf
+    x[2, cols // 2] = np.nan
+    x[3, 1:] = -np.inf
+    if dtype == "bf16":
+        bits = (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)   # exact: x holds bf16 values
+        xin, ref_in = bits, synth.bits_to_f64(bits, "bf16")
+    else:
+        xin, ref_in = x, x.astype(np.float64)
+    y = run_gpu(xin, dtype)
+    ref = softmax_rows_ref(ref_in)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+    assert np.all(y[0, ::3] == 0.0)
+    assert abs(y[3, 0] - 1.0) <= 1e-6 and np.all(y[3, 1:] == 0.0)
+    check(y, ref, dtype, f"-inf/NaN rows {dtype} cols={cols}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("cols", [1554, 2048, 20000, 70000])
+def test_large_magnitudes(dtype, cols):
+    """Values of size ~1e4 on every path (element-wise, one wave per row, one
+    workgroup per row, segments):
+    the maximum shift keeps every exponent finite, and the rounding of the
+    scaled maximum must cancel between numerators and denominator (else the
+    relative error reaches ulp(1e4 * log2 e) ~ 1e-3)."""
+    x = (synth.make_softmax_input(8, cols, "fp32", seed=3) * 3000.0).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.round_bits(x, "bf16")
+    y = run_gpu(x, dtype)
+    ref = softmax_rows_ref(synth.softmax_to_f64(x, dtype))
+    assert np.all(np.isfinite(y))
+    assert np.array_equal(np.argmax(y, axis=1), np.argmax(ref, axis=1))
+    check(y, ref, dtype, f"large magnitudes {dtype} cols={cols}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(synth.SOFTMAX_WORKLOADS))
+def test_workloads_sampled(name):
+    """The measured workloads, checked on sampled rows (plus first and last)."""
+    w = synth.SOFTMAX_WORKLOADS[name]
+    x = synth.make_softmax_workload(w)
+    y = run_gpu(x, w.dtype)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, w.rows - 1], rng.integers(0, w.rows, 64)]))
+    ref = softmax_rows_ref(synth.softmax_to_f64(x[rows], w.dtype))
+    check(y[rows], ref, w.dtype, f"workload {name} {w.describe()}")
+    assert np.all(np.isfinite(y))

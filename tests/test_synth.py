@@ -71,3 +71,40 @@ def test_to_torch_same_bits():
     t = synth.to_torch(q, "fp16")
     assert t.dtype == torch.float16
     assert np.array_equal(t.view(torch.int16).numpy().view(np.uint16), q)
+
+
+def test_softmax_input_deterministic_and_typed():
+    a = synth.make_softmax_input(5, 33, "bf16", seed=4)
+    b = synth.make_softmax_input(5, 33, "bf16", seed=4)
+    assert a.dtype == np.uint16 and a.shape == (5, 33)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, synth.make_softmax_input(5, 33, "bf16", seed=5))
+    f = synth.make_softmax_input(5, 33, "fp32", seed=4)
+    assert f.dtype == np.float32
+    # the 16-bit input is the fp32 draw rounded to nearest even
+    assert np.array_equal(a, synth.round_bits(f, "bf16"))
+    # the softmax stream is not the Q/K/V streams
+    q = synth.draw(synth.N03, 5 * 33, 4, synth.TENSOR_IDS["q"])
+    assert not np.array_equal(q.reshape(5, 33), f)
+
+
+def test_softmax_widening_is_exact():
+    bits = synth.make_softmax_input(4, 40, "fp16", seed=1)
+    x64 = synth.softmax_to_f64(bits, "fp16")
+    assert np.array_equal(x64.astype(np.float16).view(np.uint16), bits)
+    t = synth.softmax_to_torch(bits, "fp16")
+    assert np.array_equal(t.view(__import__("torch").int16).numpy().view(np.uint16), bits)
+    f = synth.make_softmax_input(3, 7, "fp32")
+    assert np.array_equal(synth.softmax_to_f64(f, "fp32"), f.astype(np.float64))
+
+
+def test_softmax_workloads():
+    for name, w in synth.SOFTMAX_WORKLOADS.items():
+        assert w.name == name and w.rows > 0 and w.cols > 0
+        assert w.elem_bytes == (4 if w.dtype == "fp32" else 2)
+    # the three kernel paths: rows within one wave's registers, rows of a
+    # workgroup, and rows whose byte length is not a multiple of 16
+    sizes = {n: w.cols * w.elem_bytes for n, w in synth.SOFTMAX_WORKLOADS.items()}
+    assert sizes["scores"] <= 16384 and sizes["scores"] % 16 == 0
+    assert 16384 < sizes["wide"] <= 262144 and sizes["wide"] % 16 == 0
+    assert sizes["odd"] % 16 != 0

@@ -1,4 +1,5 @@
-"""Python binding of the C ABI in include/attn.h (ctypes; marshalling only).
+"""Python binding of the C ABI in include/attn.h and include/softmax.h
+(ctypes; marshalling only).
 
 Every step of the attention forward pass runs in the HIP library
 ``libttc_attn.so``; this module only turns tensors into pointers, sizes and
@@ -10,13 +11,15 @@ Entry points (same names as the C functions):
 * ``attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None)``
 * ``attn_fwd_bf16(...)`` / ``attn_fwd_fp16(...)`` (same arguments, no dtype)
 * ``attn_status_str(code)``, ``attn_last_error()``, ``attn_block_rows(d)``
+* ``softmax_rows(x, y, rows, cols, dtype, stream=None)`` (row-wise softmax)
 
 ``q, k, v, o, lse`` are torch tensors on the GPU (or raw device addresses as
 ints).  ``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` int, or
 None for torch's current stream on the tensors' device.
 
 ``fwd(q, k, v, causal, scale)`` allocates ``o`` (fp32) and ``lse`` (fp32)
-with torch and calls ``attn_fwd``.
+with torch and calls ``attn_fwd``; ``softmax(x)`` allocates ``y`` like ``x``
+(a 2-D fp32/bf16/fp16 tensor) and calls ``softmax_rows``.
 """
 
 from __future__ import annotations
@@ -28,6 +31,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttc_attn
 
 ATTN_BF16 = 0
 ATTN_FP16 = 1
+
+SOFTMAX_F32 = 0
+SOFTMAX_BF16 = 1
+SOFTMAX_FP16 = 2
 
 STATUS = {
     0: "ATTN_OK",
@@ -43,7 +50,7 @@ STATUS = {
 }
 
 EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_status_str",
-           "attn_last_error", "attn_block_rows"]
+           "attn_last_error", "attn_block_rows", "softmax_rows"]
 
 
 class AttnError(RuntimeError):
@@ -79,6 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_block_rows.argtypes = [ctypes.c_int]
     lib.attn_block_rows.restype = ctypes.c_int
+    lib.softmax_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    lib.softmax_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -175,3 +185,33 @@ def fwd(q, k, v, causal: bool, scale: float, stream=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, o, lse, B, H, N, d, bool(causal), scale, stream)
     return o, lse
+
+
+def _softmax_dtype(x):
+    import torch
+
+    codes = {torch.float32: SOFTMAX_F32, torch.bfloat16: SOFTMAX_BF16, torch.float16: SOFTMAX_FP16}
+    if x.dtype not in codes:
+        raise TypeError(f"x must be float32, bfloat16 or float16, got {x.dtype}")
+    return codes[x.dtype]
+
+
+def softmax_rows(x, y, rows, cols, dtype=None, stream=None) -> None:
+    """Enqueue the row-wise softmax of [rows, cols] x into y (see include/softmax.h)."""
+    lib = load_library()
+    if dtype is None:
+        if isinstance(x, int):
+            raise TypeError("dtype is required when x is a raw address")
+        dtype = _softmax_dtype(x)
+    _check(lib.softmax_rows(_ptr(x), _ptr(y), int(rows), int(cols), int(dtype), _stream_handle(stream, x)))
+
+
+def softmax(x, stream=None):
+    """Row-wise softmax of a contiguous 2-D GPU tensor; returns a new tensor like x."""
+    import torch
+
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    y = torch.empty_like(x)
+    softmax_rows(x, y, x.shape[0], x.shape[1], _softmax_dtype(x), stream)
+    return y

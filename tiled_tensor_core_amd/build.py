@@ -20,7 +20,8 @@ LIB_NAME = "libttc_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "attn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "softmax_kernel.hip"),
+           os.path.join(CSRC, "attn_api.cpp")]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -8,7 +8,9 @@
 #include <string>
 
 #include "../../include/attn.h"
+#include "../../include/softmax.h"
 #include "attn_launch.h"
+#include "softmax_launch.h"
 
 namespace {
 
@@ -83,9 +85,31 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   return ATTN_OK;
 }
 
+int run_softmax(const void* x, void* y, int rows, int cols, int dtype, void* stream) {
+  if (dtype != SOFTMAX_F32 && dtype != SOFTMAX_BF16 && dtype != SOFTMAX_FP16) return ATTN_ERR_DTYPE;
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (rows < 1 || cols < 1) return ATTN_ERR_SHAPE;
+  const long long esize = dtype == SOFTMAX_F32 ? 4 : 2;
+  // a row is addressed with 32-bit byte offsets; the matrix with 64-bit ones
+  if ((long long)cols * esize > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const long long bytes = (long long)rows * cols * esize;
+  if (misaligned(x) || misaligned(y)) return ATTN_ERR_ALIGN;
+  if (x != y && overlaps(x, (size_t)bytes, y, (size_t)bytes)) return ATTN_ERR_ALIAS;
+  hipError_t e = ttc_sm::launch_softmax(dtype, x, y, rows, cols, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int softmax_rows(const void* x, void* y, int rows, int cols, int dtype, void* stream) {
+  return run_softmax(x, y, rows, cols, dtype, stream);
+}
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
                   int N, int d, int causal, float scale, void* stream) {

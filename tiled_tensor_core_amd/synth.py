@@ -14,11 +14,13 @@ Recipe (the same on every machine and numpy version):
   (``r = sqrt(-2 ln u1)``, ``z0 = r cos(2 pi u2)``, ``z1 = r sin(2 pi u2)``),
   uniform U(-1, 1) draws are ``2u - 1``;
 * values are scaled by the standard deviation, cast to float32, then rounded
-  to bf16 or fp16 with round-to-nearest-even.
+  to bf16 or fp16 with round-to-nearest-even (fp32 inputs keep the float32).
 
 The attention workloads below are the shapes the FlashAttention forward
 pass is measured and checked on (head dims 64 and 128, bf16 and fp16,
-causal and not, one ragged length).
+causal and not, one ragged length).  The row-softmax workloads are matrices
+of attention-score-like rows (N(0, 3^2) values): a bf16 score block, fp32
+rows too long for registers, and fp16 rows of odd length.
 """
 
 from __future__ import annotations
@@ -27,7 +29,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "x": 3}
 
 
 @dataclass(frozen=True)
@@ -157,3 +159,55 @@ def to_torch(bits: np.ndarray, dtype: str, device="cpu"):
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
     t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
     return t.to(device) if device != "cpu" else t
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    rows: int
+    cols: int
+    dtype: str          # "fp32", "bf16" or "fp16"
+    dist: Dist
+    seed: int = 0
+
+    def describe(self) -> str:
+        return f"rows={self.rows},cols={self.cols},{self.dtype}"
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
+
+
+SOFTMAX_WORKLOADS = {
+    # the score matrices of 16 heads for a 2048-token sequence (16 * 2048 rows of 2048 keys), bf16
+    "scores": SoftmaxWorkload("scores", 32768, 2048, "bf16", N03),
+    # fp32 rows of 256 KiB: longer than a wave's registers
+    "wide": SoftmaxWorkload("wide", 512, 65536, "fp32", N03),
+    # fp16 rows of odd length: no 16-byte alignment of rows
+    "odd": SoftmaxWorkload("odd", 4096, 1001, "fp16", N03),
+}
+
+
+def make_softmax_input(rows: int, cols: int, dtype: str, dist: Dist = N03, seed: int = 0) -> np.ndarray:
+    """[rows, cols] input: float32 values for "fp32", else uint16 storage bits."""
+    x = draw(dist, rows * cols, seed, TENSOR_IDS["x"]).reshape(rows, cols)
+    return x if dtype == "fp32" else round_bits(x, dtype).reshape(rows, cols)
+
+
+def make_softmax_workload(w: SoftmaxWorkload) -> np.ndarray:
+    return make_softmax_input(w.rows, w.cols, w.dtype, w.dist, w.seed)
+
+
+def softmax_to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of a softmax input (float32 values or 16-bit bits) to float64."""
+    return np.asarray(x, dtype=np.float64) if dtype == "fp32" else bits_to_f64(x, dtype)
+
+
+def softmax_to_torch(x: np.ndarray, dtype: str, device="cpu"):
+    """Softmax input -> torch tensor of the matching dtype (same values)."""
+    import torch
+
+    if dtype == "fp32":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        return t.to(device) if device != "cpu" else t
+    return to_torch(x, dtype, device)
