@@ -122,14 +122,17 @@ def time_launches(torch, launch, stream, steps, warmup, warmup_s=WARMUP_MIN_S):
     }
 
 
-def time_workload(attn, torch, w, causal, steps, warmup, inputs, warmup_s=WARMUP_MIN_S):
+def time_workload(attn, torch, w, causal, steps, warmup, inputs, warmup_s=WARMUP_MIN_S, cfg=None):
     q, k, v = inputs
     B, H, N, d = w.B, w.H, w.N, w.d
     o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    r = time_launches(torch, lambda: attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream),
-                      stream, steps, warmup, warmup_s)
+    if cfg is None:
+        launch = lambda: attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream)
+    else:
+        launch = lambda: attn.attn_fwd_cfg(q, k, v, o, lse, B, H, N, d, causal, w.scale, stream, cfg=cfg)
+    r = time_launches(torch, launch, stream, steps, warmup, warmup_s)
     r["flops"] = flops(B, H, N, d, causal)
     return r
 
@@ -280,6 +283,9 @@ def main():
     ap.add_argument("--kernel", choices=["attention", "softmax"], default="attention",
                     help="which entry point to time (default: the attention forward pass)")
     ap.add_argument("--softmax-workload", default="scores")
+    ap.add_argument("--tuned", action="store_true",
+                    help="run attention with the launch configuration cached by tiled_tensor_core_amd.tune "
+                         "for this workload (attn_fwd_cfg) instead of the built-in one (attn_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warmup-seconds", type=float, default=WARMUP_MIN_S,
                     help="minimum warm-up time in seconds (0: exactly --warmup steps, as counter runs want)")
@@ -326,7 +332,15 @@ def main():
     inputs = tuple(synth.to_torch(x, w.dtype, "cuda") for x in bits)
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
-    r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs, a.warmup_seconds)
+    cfg = None
+    if a.tuned:
+        from tiled_tensor_core_amd import tune
+
+        cfg = tune.lookup(w.dtype, w.d, causal, w.B * w.H, w.N)
+        if cfg is None:
+            print(f"[bench] no cached launch configuration for {w.name}; using the built-in one",
+                  file=sys.stderr, flush=True)
+    r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs, a.warmup_seconds, cfg)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     # the committed counter summary covers the causal B=8 H=32 N=2048 d=128 run
@@ -348,6 +362,7 @@ def main():
             "workload": f"attention fwd {'causal' if causal else 'non-causal'} {w.describe()}",
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
             "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+            "launch": (f"tuned {list(cfg.as_tuple())}" if cfg is not None else "built-in"),
         },
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
         "roofline": {

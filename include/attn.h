@@ -64,7 +64,8 @@ enum attn_status {
   ATTN_ERR_HIP = 6,            /* the kernel launch failed (see attn_last_error) */
   ATTN_ERR_SCALE = 7,          /* scale is NaN or infinite                       */
   ATTN_ERR_CAUSAL = 8,         /* causal is not 0 or 1                           */
-  ATTN_ERR_ALIAS = 9           /* o or lse overlaps another buffer               */
+  ATTN_ERR_ALIAS = 9,          /* o or lse overlaps another buffer               */
+  ATTN_ERR_CONFIG = 10         /* a launch configuration field is out of range   */
 };
 
 enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
@@ -82,6 +83,55 @@ int attn_fwd_fp16(const void* q, const void* k, const void* v, float* o, float* 
  * (ATTN_BF16 or ATTN_FP16). */
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int H, int N, int d, int causal, float scale, void* stream, int dtype);
+
+/* Launch configuration of the attention kernel.
+ *
+ * The tutorial's sections on schedule exploration and on autotuning build
+ * several configurations of a kernel, benchmark each, check its output and
+ * keep the fastest per workload.  The tile of this kernel (128 query rows x
+ * 64 keys x d) is fixed by its hand-written instruction schedule, so the
+ * configuration here is the launch schedule around that tile:
+ *
+ *   n_dom   head domains: 8 splits the B*H heads into 8 equal sets, one per
+ *           XCD, so a head's K and V stay in one L2 (needs B*H % 8 == 0);
+ *           1 lets every workgroup take items of any head.
+ *   n_work  persistent workgroups per domain, 1 .. ATTN_MAX_WORKGROUPS;
+ *           more than the domain's items (B*H/n_dom * ceil(N/128)) are
+ *           clamped to that count.
+ *   grp     heads per group in a domain's item order (items are listed
+ *           group by group, longest first within a group); clamped to the
+ *           heads of a domain.
+ *   prio    ATTN_PRIO_ON: each workgroup raises its wave priority while it
+ *           is behind on its item list, so the two workgroups sharing a
+ *           compute unit finish together; ATTN_PRIO_OFF: constant priority.
+ *
+ * A field of 0 (ATTN_PRIO_DEFAULT for prio) takes the built-in choice.  The
+ * configuration changes only which workgroup computes which (head, query
+ * block) item and in what order, never an item's arithmetic: every valid
+ * configuration gives bit-identical o and lse. */
+#define ATTN_MAX_WORKGROUPS (1 << 20)
+enum attn_prio { ATTN_PRIO_DEFAULT = 0, ATTN_PRIO_ON = 1, ATTN_PRIO_OFF = 2 };
+
+typedef struct attn_launch_cfg {
+  int n_dom;
+  int n_work;
+  int grp;
+  int prio;
+} attn_launch_cfg;
+
+/* attn_fwd with an explicit launch configuration; cfg NULL is attn_fwd.
+ * The caller owns cfg; it is read during the call only.  A field out of
+ * range returns ATTN_ERR_CONFIG before any HIP call. */
+int attn_fwd_cfg(const void* q, const void* k, const void* v, float* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale, void* stream, int dtype,
+                 const attn_launch_cfg* cfg);
+
+/* Resolve a configuration for a shape on the current device, in place:
+ * fields of 0 become the built-in choice, the others are clamped as
+ * attn_fwd_cfg would clamp them.  Queries the device's occupancy (one HIP
+ * call, cached per device); enqueues nothing.  Returns an attn_status code
+ * (ATTN_ERR_HIP if the device query fails). */
+int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_launch_cfg* cfg);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* attn_status_str(int status);

@@ -2,6 +2,7 @@
 declares, and rejects every invalid argument on the host with its status
 code before any HIP call (so no GPU is needed)."""
 
+import ctypes
 import math
 import os
 import re
@@ -29,6 +30,9 @@ def _call(fn="attn_fwd", dtype=0, **over):
             a["causal"], a["scale"], None)
     if fn == "attn_fwd":
         return lib.attn_fwd(*args, dtype)
+    if fn == "attn_fwd_cfg":
+        cfg = over.get("cfg")
+        return lib.attn_fwd_cfg(*args, dtype, ctypes.byref(cfg) if cfg is not None else None)
     return getattr(lib, fn)(*args)
 
 
@@ -62,7 +66,7 @@ def test_library_is_built_for_gfx950():
     assert targets == {b"hipv4-amdgcn-amd-amdhsa--gfx950"}
 
 
-@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16"])
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg"])
 @pytest.mark.parametrize("over,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 16, H=1 << 16), 2),
@@ -138,3 +142,43 @@ def test_softmax_rejects_invalid_arguments(over, code):
     a.update(over)
     lib = attn.load_library()
     assert lib.softmax_rows(a["x"], a["y"], a["rows"], a["cols"], a["dtype"], None) == code
+
+
+BAD_CFGS = [  # (n_dom, n_work, grp, prio)
+    (2, 0, 0, 0), (-1, 0, 0, 0), (16, 0, 0, 0), (0, -1, 0, 0), (0, (1 << 20) + 1, 0, 0),
+    (0, 0, -3, 0), (0, 0, 0, 3), (0, 0, 0, -1),
+]
+
+
+@pytest.mark.parametrize("fields", BAD_CFGS, ids=str)
+def test_cfg_rejects_out_of_range_fields(fields):
+    """Checked on the host before any HIP call (no GPU here)."""
+    cfg = attn.LaunchCfg(*fields)
+    assert _call("attn_fwd_cfg", cfg=cfg) == 10
+    assert attn.load_library().attn_resolve_cfg(2, 4, 256, 64, 0, 0, ctypes.byref(cfg)) == 10
+
+
+def test_cfg_eight_domains_need_heads_divisible_by_eight():
+    cfg = attn.LaunchCfg(n_dom=8)
+    assert _call("attn_fwd_cfg", B=1, H=3, cfg=cfg) == 10
+    lib = attn.load_library()
+    assert lib.attn_resolve_cfg(1, 3, 256, 64, 0, 0, ctypes.byref(cfg)) == 10
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 4, 256, 64, 0, 0), 2), ((2, 0, 256, 64, 0, 0), 2), ((2, 4, 0, 64, 0, 0), 2),
+    ((2, 4, 256, 96, 0, 0), 3), ((2, 4, 256, 64, 2, 0), 8), ((2, 4, 256, 64, 0, 7), 5),
+])
+def test_resolve_cfg_rejects_invalid_shapes(args, code):
+    cfg = attn.LaunchCfg()
+    assert attn.load_library().attn_resolve_cfg(*args, ctypes.byref(cfg)) == code
+
+
+def test_resolve_cfg_rejects_null():
+    assert attn.load_library().attn_resolve_cfg(2, 4, 256, 64, 0, 0, None) == 1
+
+
+def test_cfg_forms():
+    assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1)
+    assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0)
+    assert attn._cfg(None) is None

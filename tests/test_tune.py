@@ -1,0 +1,99 @@
+"""Launch-configuration search (tiled_tensor_core_amd/tune.py).
+
+CPU: the cache helpers.  GPU: every candidate configuration gives O and LSE
+bit-identical to the built-in configuration (which the parity tests check
+against the oracle), on shapes with 8 head domains, with a single domain,
+causal and not, with a ragged last query block; and a search on a small
+workload writes a cache entry that fwd_tuned then uses.
+"""
+
+import json
+
+import pytest
+
+from tiled_tensor_core_amd import attn, synth, tune
+from parity import gpu_available
+
+
+def test_cache_roundtrip(tmp_path):
+    path = str(tmp_path / "cache.json")
+    assert tune.lookup("bf16", 128, True, 256, 2048, path) is None
+    key = tune.cache_key("bf16", 128, True, 256, 2048)
+    assert key == "bf16/d128/causal/BH256/N2048"
+    tune.store(key, {"cfg": [8, 64, 4, 1], "us": 1.0, "first_pass": [1, 2]}, path)
+    tune.store(tune.cache_key("fp16", 64, False, 12, 100), {"cfg": [1, 5, 2, 2], "us": 2.0}, path)
+    data = json.load(open(path))
+    assert set(data) == {key, "fp16/d64/full/BH12/N100"}
+    assert "first_pass" not in data[key]
+    assert tune.lookup("bf16", 128, True, 256, 2048, path).as_tuple() == (8, 64, 4, 1)
+    assert tune.lookup("fp16", 64, False, 12, 100, path).as_tuple() == (1, 5, 2, 2)
+    assert tune.lookup("fp16", 64, True, 12, 100, path) is None
+
+
+def test_committed_cache_entries_are_well_formed():
+    for key, e in tune.load_cache().items():
+        dtype, d, mode, bh, n = key.split("/")
+        assert dtype in ("bf16", "fp16") and d in ("d64", "d128") and mode in ("causal", "full")
+        n_dom, n_work, grp, prio = e["cfg"]
+        assert n_dom in (1, 8) and n_work >= 1 and grp >= 1 and prio in (1, 2)
+        assert e["us"] > 0 and e["default_us"] > 0
+
+
+def _inputs(B, H, N, d, dtype, seed):
+    q, k, v = synth.make_qkv(B, H, N, d, dtype, seed=seed)
+    return tuple(synth.to_torch(x, dtype, "cuda") for x in (q, k, v))
+
+
+SHAPES = [  # B, H, N, d, dtype: 8 domains; 1 domain (B*H % 8 != 0); ragged N
+    (2, 8, 1024, 64, "bf16"), (1, 6, 700, 128, "bf16"), (3, 5, 333, 64, "fp16"), (2, 4, 2048, 128, "fp16"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d,dtype", SHAPES)
+def test_every_candidate_is_bit_identical(B, H, N, d, dtype, causal):
+    import torch
+
+    q, k, v = _inputs(B, H, N, d, dtype, seed=N)
+    code = attn.ATTN_BF16 if dtype == "bf16" else attn.ATTN_FP16
+    scale = d ** -0.5
+    o0, l0 = attn.fwd(q, k, v, causal, scale)
+    cands = tune.candidates(B, H, N, d, causal, code)
+    assert cands[0].as_tuple() == attn.attn_resolve_cfg(B, H, N, d, causal, code).as_tuple()
+    print(f"[tune] {B},{H},{N},{d} {dtype} causal={causal}: {len(cands)} configurations", flush=True)
+    for c in cands:
+        o, lse = attn.fwd(q, k, v, causal, scale, cfg=c)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(lse, l0), f"{c} changed the output"
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")
+def test_resolved_builtin_configuration():
+    c = attn.attn_resolve_cfg(8, 32, 2048, 128, 1, attn.ATTN_BF16)
+    items_per_dom = 8 * 32 * 16 // c.n_dom
+    assert c.n_dom == 8 and 1 <= c.n_work <= items_per_dom and c.grp >= 1 and c.prio == attn.ATTN_PRIO_ON
+    c1 = attn.attn_resolve_cfg(1, 3, 500, 64, 0, attn.ATTN_FP16)
+    assert c1.n_dom == 1 and c1.n_work <= 3 * 4 and c1.grp <= 3
+    # explicit fields are kept, within what the shape allows
+    c2 = attn.attn_resolve_cfg(8, 32, 2048, 128, 1, attn.ATTN_BF16, attn.LaunchCfg(1, 10 ** 6, 1000, 2))
+    assert c2.as_tuple() == (1, 8 * 32 * 16, 8 * 32, 2)
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")
+def test_search_writes_a_validated_cache_entry(tmp_path):
+    import torch
+
+    path = str(tmp_path / "cache.json")
+    q, k, v = _inputs(4, 16, 1024, 64, "bf16", seed=3)
+    r = tune.tune(q, k, v, True, 0.125, reps=3, top=3, rounds=2, warm_s=0.1, cache_path=path)
+    assert r["us"] <= r["default_us"] * 1.0001
+    cfg = tune.lookup("bf16", 64, True, 64, 1024, path)
+    assert cfg is not None and list(cfg.as_tuple()) == r["cfg"]
+    o0, l0 = attn.fwd(q, k, v, True, 0.125)
+    o1, l1 = tune.fwd_tuned(q, k, v, True, 0.125, cache_path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)

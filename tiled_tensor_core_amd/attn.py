@@ -47,10 +47,29 @@ STATUS = {
     7: "ATTN_ERR_SCALE",
     8: "ATTN_ERR_CAUSAL",
     9: "ATTN_ERR_ALIAS",
+    10: "ATTN_ERR_CONFIG",
 }
 
-EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_status_str",
-           "attn_last_error", "attn_block_rows", "softmax_rows"]
+ATTN_PRIO_DEFAULT = 0
+ATTN_PRIO_ON = 1
+ATTN_PRIO_OFF = 2
+ATTN_MAX_WORKGROUPS = 1 << 20
+
+
+class LaunchCfg(ctypes.Structure):
+    """attn_launch_cfg of include/attn.h (a field of 0 takes the built-in choice)."""
+
+    _fields_ = [("n_dom", ctypes.c_int), ("n_work", ctypes.c_int), ("grp", ctypes.c_int),
+                ("prio", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.n_dom, self.n_work, self.grp, self.prio)
+
+    def __repr__(self):
+        return f"LaunchCfg(n_dom={self.n_dom}, n_work={self.n_work}, grp={self.grp}, prio={self.prio})"
+
+EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg", "attn_resolve_cfg",
+           "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows"]
 
 
 class AttnError(RuntimeError):
@@ -80,6 +99,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.attn_fwd.argtypes = fwd_args + [ctypes.c_int]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_cfg.argtypes = fwd_args + [ctypes.c_int, ctypes.POINTER(LaunchCfg)]
+    lib.attn_fwd_cfg.restype = ctypes.c_int
+    lib.attn_resolve_cfg.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(LaunchCfg)]
+    lib.attn_resolve_cfg.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -148,6 +171,34 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None
     _check(lib.attn_fwd(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream), code))
 
 
+def _cfg(cfg) -> LaunchCfg | None:
+    if cfg is None or isinstance(cfg, LaunchCfg):
+        return cfg
+    if isinstance(cfg, dict):
+        return LaunchCfg(**cfg)
+    return LaunchCfg(*cfg)
+
+
+def attn_fwd_cfg(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None, cfg=None) -> None:
+    """attn_fwd with a launch configuration (LaunchCfg, a 4-tuple or a dict; None: built-in)."""
+    lib = load_library()
+    if dtype is None and isinstance(q, int):
+        raise TypeError("dtype is required when q is a raw address")
+    code = _dtype_code(q, dtype)
+    c = _cfg(cfg)
+    _check(lib.attn_fwd_cfg(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream), code,
+                            ctypes.byref(c) if c is not None else None))
+
+
+def attn_resolve_cfg(B, H, N, d, causal, dtype, cfg=None) -> LaunchCfg:
+    """The configuration attn_fwd_cfg would run for this shape (fields of 0 resolved)."""
+    lib = load_library()
+    c = _cfg(cfg) or LaunchCfg()
+    c = LaunchCfg(*c.as_tuple())
+    _check(lib.attn_resolve_cfg(int(B), int(H), int(N), int(d), int(causal), int(dtype), ctypes.byref(c)))
+    return c
+
+
 def attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
     lib = load_library()
     _check(lib.attn_fwd_bf16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream)))
@@ -170,8 +221,9 @@ def attn_block_rows(d: int) -> int:
     return int(load_library().attn_block_rows(int(d)))
 
 
-def fwd(q, k, v, causal: bool, scale: float, stream=None):
-    """O (fp32) and LSE (fp32) for [B, H, N, d] tensors q, k, v on the GPU."""
+def fwd(q, k, v, causal: bool, scale: float, stream=None, cfg=None):
+    """O (fp32) and LSE (fp32) for [B, H, N, d] tensors q, k, v on the GPU
+    (cfg: an optional launch configuration, see attn_fwd_cfg)."""
     import torch
 
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -183,7 +235,10 @@ def fwd(q, k, v, causal: bool, scale: float, stream=None):
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, B, H, N, d, bool(causal), scale, stream)
+    if cfg is None:
+        attn_fwd(q, k, v, o, lse, B, H, N, d, bool(causal), scale, stream)
+    else:
+        attn_fwd_cfg(q, k, v, o, lse, B, H, N, d, bool(causal), scale, stream, cfg=cfg)
     return o, lse
 
 

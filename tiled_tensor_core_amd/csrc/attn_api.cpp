@@ -23,8 +23,19 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Fields of a caller's launch configuration: 0 (built-in choice) or in range.
+bool cfg_valid(const attn_launch_cfg* c, long long bh) {
+  if (!c) return true;
+  if (c->n_dom != 0 && c->n_dom != 1 && c->n_dom != 8) return false;
+  if (c->n_dom == 8 && bh % 8 != 0) return false;
+  if (c->n_work < 0 || c->n_work > ATTN_MAX_WORKGROUPS) return false;
+  if (c->grp < 0) return false;
+  if (c->prio != ATTN_PRIO_DEFAULT && c->prio != ATTN_PRIO_ON && c->prio != ATTN_PRIO_OFF) return false;
+  return true;
+}
+
 int run(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N,
-        int d, int causal, float scale, void* stream, int dtype) {
+        int d, int causal, float scale, void* stream, int dtype, const attn_launch_cfg* user_cfg) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
@@ -38,6 +49,7 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   // one head's K, V or O is addressed with 32-bit byte offsets (O: fp32,
   // with room for the rows of a ragged last block of 128)
   if ((long long)(N + 128) * d * 4 > 0xffffffffLL) return ATTN_ERR_SHAPE;
+  if (!cfg_valid(user_cfg, bh)) return ATTN_ERR_CONFIG;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return ATTN_ERR_ALIGN;
   const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4,
@@ -76,8 +88,11 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
     prm.q_mode = 2;
   }
 
-  hipError_t e = ttc::launch_attn_fwd(dtype == ATTN_BF16, d, causal == 1, prm,
-                                      static_cast<hipStream_t>(stream));
+  ttc::LaunchCfg cfg{};
+  if (user_cfg) cfg = {user_cfg->n_dom, user_cfg->n_work, user_cfg->grp, user_cfg->prio};
+  hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, cfg);
+  if (e == hipSuccess)
+    e = ttc::launch_attn_fwd(dtype == ATTN_BF16, d, causal == 1, prm, cfg, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = hipGetErrorString(e);
     return ATTN_ERR_HIP;
@@ -113,17 +128,48 @@ int softmax_rows(const void* x, void* y, int rows, int cols, int dtype, void* st
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
                   int N, int d, int causal, float scale, void* stream) {
-  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_BF16);
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_BF16, nullptr);
 }
 
 int attn_fwd_fp16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
                   int N, int d, int causal, float scale, void* stream) {
-  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_FP16);
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_FP16, nullptr);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
              int N, int d, int causal, float scale, void* stream, int dtype) {
-  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype);
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype, nullptr);
+}
+
+int attn_fwd_cfg(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+                 int N, int d, int causal, float scale, void* stream, int dtype,
+                 const attn_launch_cfg* cfg) {
+  return run(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype, cfg);
+}
+
+int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_launch_cfg* cfg) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (!cfg) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+  if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 30) || bh * N > (1LL << 40)) return ATTN_ERR_SHAPE;
+  if (!cfg_valid(cfg, bh)) return ATTN_ERR_CONFIG;
+  ttc::AttnParams prm{};
+  prm.BH = (int)bh;
+  prm.N = N;
+  ttc::LaunchCfg c{cfg->n_dom, cfg->n_work, cfg->grp, cfg->prio};
+  const hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, c);
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  cfg->n_dom = c.n_dom;
+  cfg->n_work = c.n_work;
+  cfg->grp = c.grp;
+  cfg->prio = c.prio;
+  return ATTN_OK;
 }
 
 const char* attn_status_str(int status) {
@@ -138,6 +184,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_CAUSAL: return "causal must be 0 or 1";
     case ATTN_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
+    case ATTN_ERR_CONFIG: return "launch configuration field out of range";
     default: return "unknown status";
   }
 }

@@ -630,7 +630,9 @@ attn_fwd_kernel(AttnParams p) {
     if (!item(t, b2, q2)) break;
     tot_tiles += tiles_of(q2);
   }
-  const int th1 = tot_tiles / 2, th2 = (3 * tot_tiles) / 4, th3 = (9 * tot_tiles) / 10;
+  // with the priority scheme off every threshold is 0: the priority stays 0
+  const int th1 = p.prio ? tot_tiles / 2 : 0, th2 = p.prio ? (3 * tot_tiles) / 4 : 0,
+            th3 = p.prio ? (9 * tot_tiles) / 10 : 0;
   int done_tiles = 0;
   auto progress = [&]() {
     ++done_tiles;
@@ -904,7 +906,34 @@ static int resident_groups(int variant, const void* fn) {
   return n;
 }
 
-hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, hipStream_t stream) {
+static const void* variant_fn(bool bf16, int d, bool causal) {
+  return bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true>() : kernel_fn<true, 64, false>())
+                         : (causal ? kernel_fn<true, 128, true>() : kernel_fn<true, 128, false>()))
+              : (d == 64 ? (causal ? kernel_fn<false, 64, true>() : kernel_fn<false, 64, false>())
+                         : (causal ? kernel_fn<false, 128, true>() : kernel_fn<false, 128, false>()));
+}
+
+hipError_t resolve_cfg(bool bf16, int d, bool causal, const AttnParams& prm, LaunchCfg& cfg) {
+  const long long n_qblk = (prm.N + block_rows(d) - 1) / block_rows(d);
+  const long long items = (long long)prm.BH * n_qblk;
+  const int variant = (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
+  const int slots = resident_groups(variant, variant_fn(bf16, d, causal));
+  if (slots < 0) return hipErrorInvalidDevice;
+  // built-in: heads split over the 8 XCDs when they divide evenly, as many
+  // workgroups as run at once, groups of heads that fill one round of items
+  if (cfg.n_dom == 0) cfg.n_dom = (prm.BH % 8 == 0) ? 8 : 1;
+  if (cfg.n_dom == 8 && prm.BH % 8 != 0) cfg.n_dom = 1;
+  const long long per_dom = items / cfg.n_dom;
+  if (cfg.n_work == 0) cfg.n_work = std::max(1, slots / cfg.n_dom);
+  cfg.n_work = (int)std::min<long long>(cfg.n_work, per_dom);
+  if (cfg.grp == 0) cfg.grp = (int)std::max<long long>(1, cfg.n_work / n_qblk);
+  cfg.grp = std::min(cfg.grp, prm.BH / cfg.n_dom);
+  if (cfg.prio == 0) cfg.prio = 1;
+  return hipSuccess;
+}
+
+hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const LaunchCfg& cfg,
+                           hipStream_t stream) {
   const int bm = block_rows(d);
   prm.n_qblk = (prm.N + bm - 1) / bm;
   // raw-score margin before the reference maximum moves: 0 for bf16 (exact
@@ -912,23 +941,13 @@ hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, hipStr
   prm.thr = bf16 ? 0.0f : fminf(8.0f / prm.c, 3.0e38f);
   const long long items = (long long)prm.BH * prm.n_qblk;
   if (items > (1LL << 30)) return hipErrorInvalidConfiguration;
-
-  const int variant = (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
-  const void* fn = bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true>() : kernel_fn<true, 64, false>())
-                                   : (causal ? kernel_fn<true, 128, true>() : kernel_fn<true, 128, false>()))
-                        : (d == 64 ? (causal ? kernel_fn<false, 64, true>() : kernel_fn<false, 64, false>())
-                                   : (causal ? kernel_fn<false, 128, true>() : kernel_fn<false, 128, false>()));
-  const int slots = resident_groups(variant, fn);
-  if (slots < 0) return hipErrorInvalidDevice;
-  // heads split over the 8 XCDs when they divide evenly
-  prm.n_dom = (prm.BH % 8 == 0) ? 8 : 1;
-  const long long per_dom = items / prm.n_dom;
-  prm.n_work = (int)std::min<long long>(std::max(1, slots / prm.n_dom), per_dom);
-  prm.grp = std::max(1, prm.n_work / prm.n_qblk);
+  prm.n_dom = cfg.n_dom;
+  prm.n_work = cfg.n_work;
+  prm.grp = cfg.grp;
+  prm.prio = cfg.prio == 1 ? 1 : 0;
   const int grid = prm.n_dom * prm.n_work;
-
   void* args[] = {&prm};
-  return hipLaunchKernel(fn, dim3(grid), dim3(kNW * 64), args, 0, stream);
+  return hipLaunchKernel(variant_fn(bf16, d, causal), dim3(grid), dim3(kNW * 64), args, 0, stream);
 }
 
 }  // namespace ttc

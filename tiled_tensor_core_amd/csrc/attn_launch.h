@@ -20,12 +20,28 @@ struct AttnParams {
   float c;             // |scale| * log2(e), or log2(e) when scale == 0
   float thr;           // raw-score margin before the running maximum moves (set by the launcher)
   int q_mode;          // 0: use Q; 1: use -Q (negative scale); 2: use 0 (zero scale)
+  int prio;            // 1: workgroups set their wave priority by progress; 0: they do not
+};
+
+// Launch configuration; a field of 0 takes the built-in choice.
+struct LaunchCfg {
+  int n_dom;    // 1 or 8 head domains
+  int n_work;   // persistent workgroups per domain
+  int grp;      // heads per group in a domain's item order
+  int prio;     // 1 on, 2 off
 };
 
 // Query rows per workgroup for head dim d.
 int block_rows(int d);
 
-// Enqueue the kernel on `stream`.  Arguments are already validated.
-hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, hipStream_t stream);
+// Fill the launch configuration for prm's shape: fields of cfg that are 0
+// get the built-in choice, the others are clamped to what the shape allows.
+// prm.BH and prm.N must be set.  Queries the device's occupancy once.
+hipError_t resolve_cfg(bool bf16, int d, bool causal, const AttnParams& prm, LaunchCfg& cfg);
+
+// Enqueue the kernel on `stream` with a configuration resolve_cfg filled.
+// Arguments are already validated.
+hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const LaunchCfg& cfg,
+                           hipStream_t stream);
 
 }  // namespace ttc
