@@ -18,6 +18,10 @@ has passed: the GPU reaches its sustained clocks only after tens of
 milliseconds of load, and timing before that under-reports a loaded GPU by
 about 10 %.
 
+``--kernel gemm`` times ``gemm_bf16`` with the bias + GELU epilogue on the
+MLP up-projection workload (M=16384 tokens, K=4096, N=16384): 2*M*N*K FLOPs
+against the dense bf16 MFMA peak.
+
 ``--kernel softmax`` times the row-wise softmax entry point ``softmax_rows``
 instead: a step is one softmax over a [rows, cols] matrix resident in HBM,
 reported in GB/s of algorithmic traffic (each element read once and written
@@ -47,6 +51,8 @@ KERNEL_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "attn_fwd_kerne
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b8h32n2048d128_traffic.txt")
 SOFTMAX_METRIC = "row softmax GB/s (algorithmic bytes: one read and one write per element) + % of MI355X HBM peak"
 SOFTMAX_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "softmax_kernel.hip")
+GEMM_METRIC = "GEMM + bias + GELU TFLOP/s (2*M*N*K) + % of MI355X bf16 MFMA peak"
+GEMM_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "gemm_kernel.hip")
 
 
 def flops(B, H, N, d, causal):
@@ -274,15 +280,125 @@ def run_softmax(a, torch, attn, synth):
     print(json.dumps(out), flush=True)
 
 
+def gemm_cpu_baseline(w, a_bits, w_bits, bias, budget_s):
+    """The fp64 GEMM + bias + GELU oracle on blocks of 64 rows of A until
+    ``budget_s`` of CPU time has passed; TFLOP/s over 2 * rows * N * K."""
+    from oracle import EPI_BIAS_GELU, gemm_ref
+    from tiled_tensor_core_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    w64 = synth.bits_to_f64(w_bits, "bf16")
+    b64 = bias.astype(np.float64)
+    done = 0
+    elapsed = 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        for r0 in range(0, w.M, 64):
+            a64 = synth.bits_to_f64(a_bits[r0:r0 + 64], "bf16")
+            ts = time.perf_counter()
+            gemm_ref(a64, w64, b64, EPI_BIAS_GELU)
+            elapsed += time.perf_counter() - ts
+            done += a64.shape[0]
+            if elapsed >= budget_s:
+                break
+    f = 2.0 * done * w.N * w.K
+    return {
+        "value": f / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.M} rows of A (all {w.N} outputs each), fp64 numpy, "
+                  f"{elapsed:.1f} s; wall {time.perf_counter() - t0:.1f} s",
+    }
+
+
+def run_gemm(a, torch, attn, synth):
+    wl = synth.GEMM_WORKLOADS[a.gemm_workload]
+    print(f"[bench] generating GEMM inputs {wl.describe()}", file=sys.stderr, flush=True)
+    a_bits, w_bits, bias = synth.make_gemm_workload(wl)
+    at = synth.to_torch(a_bits, "bf16", "cuda")
+    wt = synth.to_torch(w_bits, "bf16", "cuda")
+    bt = torch.from_numpy(bias).cuda()
+    ct = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} GEMM steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
+    r = time_launches(torch, lambda: attn.gemm_bf16(at, wt, bt, ct, wl.M, wl.N, wl.K, attn.GEMM_EPI_BIAS_GELU,
+                                                    stream), stream, a.steps, a.warmup, a.warmup_seconds)
+    f = wl.flops()
+    value = f / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = f / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    traffic = measured_traffic(os.path.join(ROOT, "profiles", f"gemm_{wl.name}_m{wl.M}n{wl.N}k{wl.K}_traffic.txt"),
+                               GEMM_SRC)
+    out = {
+        "metric": GEMM_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gemm + bias + gelu {wl.name} {wl.describe()}", "M": wl.M, "N": wl.N, "K": wl.K,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+            "kernel_ms_median": round(r["kernel_ms_median"], 5),
+        },
+    }
+    if a.extra:
+        per = {}
+        for name, ow in synth.GEMM_WORKLOADS.items():
+            if name == wl.name:
+                continue
+            oa, ow_, ob = synth.make_gemm_workload(ow)
+            oat, owt = synth.to_torch(oa, "bf16", "cuda"), synth.to_torch(ow_, "bf16", "cuda")
+            obt = torch.from_numpy(ob).cuda()
+            oct = torch.empty((ow.M, ow.N), dtype=torch.bfloat16, device="cuda")
+            rr = time_launches(torch, lambda: attn.gemm_bf16(oat, owt, obt, oct, ow.M, ow.N, ow.K,
+                                                             attn.GEMM_EPI_BIAS_GELU, stream),
+                               stream, 20, 5, a.warmup_seconds)
+            per[f"{name} {ow.describe()}"] = round(ow.flops() / (rr["kernel_ms_median"] * 1e-3) / 1e12, 1)
+        out["per_workload_tflops"] = per
+        # context: eager PyTorch on the same inputs (the library GEMM, then the bias and GELU
+        # as separate elementwise kernels), whole-call time per step
+        import torch.nn.functional as F
+
+        rt = time_launches(torch, lambda: F.gelu(torch.addmm(bt.to(torch.bfloat16), at, wt.t())),
+                           stream, 20, 5, a.warmup_seconds)
+        out["eager_torch_tflops"] = round(f / (rt["kernel_ms_median"] * 1e-3) / 1e12, 1)
+    if not a.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{a.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = gemm_cpu_baseline(wl, a_bits, w_bits, bias, a.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama")
-    ap.add_argument("--kernel", choices=["attention", "softmax"], default="attention",
+    ap.add_argument("--kernel", choices=["attention", "softmax", "gemm"], default="attention",
                     help="which entry point to time (default: the attention forward pass)")
     ap.add_argument("--softmax-workload", default="scores")
+    ap.add_argument("--gemm-workload", default="mlp")
     ap.add_argument("--tuned", action="store_true",
                     help="run attention with the launch configuration cached by tiled_tensor_core_amd.tune "
                          "for this workload (attn_fwd_cfg) instead of the built-in one (attn_fwd)")
@@ -324,6 +440,9 @@ def main():
         torch.cuda.empty_cache()
     if a.kernel == "softmax":
         run_softmax(a, torch, attn, synth)
+        return
+    if a.kernel == "gemm":
+        run_gemm(a, torch, attn, synth)
         return
     w = synth.WORKLOADS[a.workload]
     causal = w.causal[-1]

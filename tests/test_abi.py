@@ -14,7 +14,7 @@ from tiled_tensor_core_amd import attn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
-HEADERS = [HEADER, os.path.join(ROOT, "include", "softmax.h")]
+HEADERS = [HEADER, os.path.join(ROOT, "include", "softmax.h"), os.path.join(ROOT, "include", "gemm.h")]
 
 # fake, 16-byte-aligned, well separated "device" addresses: validation never
 # dereferences them, and every case below fails validation
@@ -41,7 +41,7 @@ def declared_functions():
     for header in HEADERS:
         text = open(header).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"\b((?:attn|softmax)_[a-z0-9_]+)\s*\(", text))
+        names |= set(re.findall(r"\b((?:attn|softmax|gemm)_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT ((?:attn|softmax)_[a-z0-9_]+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT ((?:attn|softmax|gemm)_[a-z0-9_]+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -182,3 +182,29 @@ def test_cfg_forms():
     assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1)
     assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0)
     assert attn._cfg(None) is None
+
+
+GA, GW, GB, GC = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+GEMM_GOOD = dict(a=GA, w=GW, bias=GB, c=GC, M=100, N=64, K=32, epi=2)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(a=0), 1), (dict(w=0), 1), (dict(c=0), 1), (dict(bias=0), 1), (dict(bias=0, epi=1), 1),
+    (dict(M=0), 2), (dict(M=-1), 2), (dict(N=0), 2), (dict(N=12), 2), (dict(K=4), 2), (dict(K=30), 2),
+    (dict(N=4194304), 2), (dict(K=4194304), 2),
+    (dict(a=GA + 8), 4), (dict(w=GW + 2), 4), (dict(c=GC + 4), 4), (dict(bias=GB + 4), 4),
+    (dict(c=GA), 9), (dict(c=GW + 16), 9), (dict(bias=GC + 64), 9),
+    (dict(epi=3), 10), (dict(epi=-1), 10),
+])
+def test_gemm_rejects_invalid_arguments(over, code):
+    a = dict(GEMM_GOOD)
+    a.update(over)
+    lib = attn.load_library()
+    assert lib.gemm_bf16(a["a"], a["w"], a["bias"], a["c"], a["M"], a["N"], a["K"], a["epi"], None) == code
+
+
+def test_gemm_bias_may_be_null_without_a_bias_epilogue():
+    """NULL bias passes validation with GEMM_EPI_NONE: the call then fails only
+    at a later check (here: misaligned c), never on the bias."""
+    lib = attn.load_library()
+    assert lib.gemm_bf16(GA, GW, None, GC + 4, 100, 64, 32, 0, None) == 4

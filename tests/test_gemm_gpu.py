@@ -1,0 +1,113 @@
+"""GPU parity of the GEMM kernel with its fused epilogue (C ABI ``gemm_bf16``)
+against the fp64 oracle (oracle/gemm.py) on seeded inputs.
+
+Tolerance, per element: |c - c_ref| <= 2^-8 |c_ref| + 1.13 * 6 sqrt(K) 2^-24 S,
+with S = sum_k |a_k w_k| + |b|.  The first term covers the one rounding of
+the output to bf16 (half an ulp is 2^-9 relative).  The second is the
+probabilistic bound on fp32 accumulation (Higham and Mary: the error of a
+sum of K terms stays within lambda sqrt(K) u S with overwhelming
+probability; lambda = 6, u = 2^-24), times the largest slope of GELU
+(1.13).  At the measured sizes it is a few 1e-4 against outputs of order 1.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import EPI_BIAS, EPI_BIAS_GELU, EPI_NONE, gemm_ref
+from tiled_tensor_core_amd import synth
+from parity import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _run(a_bits, w_bits, bias, epi):
+    import torch
+
+    from tiled_tensor_core_amd import attn
+
+    a = synth.to_torch(a_bits, "bf16", "cuda")
+    w = synth.to_torch(w_bits, "bf16", "cuda")
+    b = torch.from_numpy(bias).cuda() if epi != EPI_NONE else None
+    c = attn.gemm(a, w, b, epilogue=epi)
+    torch.cuda.synchronize()
+    return synth.bits_to_f64(c.cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+
+
+def _check(c, a64, w64, bias, epi, tag, rows=None):
+    ref = gemm_ref(a64, w64, bias, epi)
+    S = np.abs(a64) @ np.abs(w64).T + (np.abs(bias)[None, :] if epi != EPI_NONE else 0.0)
+    K = a64.shape[1]
+    bound = 2.0 ** -8 * np.abs(ref) + 1.13 * 6.0 * np.sqrt(K) * 2.0 ** -24 * S
+    err = np.abs(c - ref)
+    worst = float(np.max(err / bound))
+    print(f"[gemm parity] {tag}: max err/bound {worst:.3f}, max abs err {float(err.max()):.3e}", flush=True)
+    assert np.all(np.isfinite(c)), f"{tag}: non-finite output"
+    assert np.all(err <= bound), f"{tag}: worst err/bound {worst}"
+
+
+SHAPES = [  # M, N, K: one partial tile; exact tiles; ragged in all three with a K tail; tiny
+    (300, 264, 200), (256, 256, 64), (512, 512, 128), (1000, 776, 328), (1, 8, 8), (17, 24, 72), (257, 8, 4104),
+]
+
+
+@pytest.mark.parametrize("epi", [EPI_NONE, EPI_BIAS, EPI_BIAS_GELU])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_parity(M, N, K, epi):
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=M + N + K)
+    c = _run(a, w, b, epi)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), epi,
+           f"{M}x{N}x{K} epi={epi}")
+
+
+def test_gelu_range_and_large_values():
+    """Pre-activations from -40 to 40 (scaled weights): both GELU tails and the
+    region around 0, where GELU bends, are exercised."""
+    M, N, K = 256, 264, 256
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=9)
+    w = synth.round_bits(synth.bits_to_f32(w, "bf16") * 16.0, "bf16")   # |z| up to ~40
+    b = (b * 4.0).astype(np.float32)
+    c = _run(a, w, b, EPI_BIAS_GELU)
+    a64, w64 = synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16")
+    z = a64 @ w64.T + b
+    assert z.min() < -20 and z.max() > 20
+    _check(c, a64, w64, b.astype(np.float64), EPI_BIAS_GELU, "wide pre-activations")
+
+
+@pytest.mark.slow
+def test_mlp_workload_sampled_rows():
+    """The measured workload at full size, checked on sampled rows (first,
+    last and 30 random) of C against the oracle."""
+    import torch
+
+    from tiled_tensor_core_amd import attn
+
+    wl = synth.GEMM_WORKLOADS["mlp"]
+    a, w, b = synth.make_gemm_workload(wl)
+    at = synth.to_torch(a, "bf16", "cuda")
+    wt = synth.to_torch(w, "bf16", "cuda")
+    c = attn.gemm(at, wt, torch.from_numpy(b).cuda(), epilogue=EPI_BIAS_GELU)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, wl.M - 1], rng.integers(0, wl.M, 30)]))
+    ct = c[torch.from_numpy(rows).cuda()].cpu()
+    cr = synth.bits_to_f64(ct.view(torch.int16).numpy().view(np.uint16), "bf16")
+    _check(cr, synth.bits_to_f64(a[rows], "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64),
+           EPI_BIAS_GELU, f"mlp {wl.describe()} sampled rows")
+    assert bool(torch.isfinite(c.float()).all())
+
+
+def test_rejects_bad_arguments_before_launch():
+    import torch
+
+    from tiled_tensor_core_amd import attn
+
+    a = torch.zeros((4, 16), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.gemm_bf16(a, w, None, c, 4, 8, 16, attn.GEMM_EPI_BIAS)
+    assert e.value.code == 1
+    with pytest.raises(attn.AttnError) as e:
+        attn.gemm_bf16(a, w, None, c, 4, 8, 12, attn.GEMM_EPI_NONE)
+    assert e.value.code == 2

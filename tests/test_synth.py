@@ -108,3 +108,16 @@ def test_softmax_workloads():
     assert sizes["scores"] <= 16384 and sizes["scores"] % 16 == 0
     assert 16384 < sizes["wide"] <= 262144 and sizes["wide"] % 16 == 0
     assert sizes["odd"] % 16 != 0
+
+
+def test_gemm_inputs():
+    a, w, b = synth.make_gemm_inputs(6, 16, 64, seed=2)
+    a2, w2, b2 = synth.make_gemm_inputs(6, 16, 64, seed=2)
+    assert a.dtype == np.uint16 and a.shape == (6, 64) and w.shape == (16, 64) and b.shape == (16,)
+    assert b.dtype == np.float32 and np.array_equal(a, a2) and np.array_equal(w, w2) and np.array_equal(b, b2)
+    # W ~ N(0, 1/K): a linear layer's initialisation scale; b ~ U(-1, 1)
+    wl = synth.bits_to_f64(synth.make_gemm_inputs(4, 256, 1024, seed=3)[1], "bf16")
+    assert abs(wl.std() * np.sqrt(1024) - 1.0) < 0.02
+    assert np.all(np.abs(b) <= 1.0)
+    for name, g in synth.GEMM_WORKLOADS.items():
+        assert g.name == name and g.N % 8 == 0 and g.K % 8 == 0 and g.flops() == 2.0 * g.M * g.N * g.K

@@ -68,8 +68,12 @@ class LaunchCfg(ctypes.Structure):
     def __repr__(self):
         return f"LaunchCfg(n_dom={self.n_dom}, n_work={self.n_work}, grp={self.grp}, prio={self.prio})"
 
+GEMM_EPI_NONE = 0
+GEMM_EPI_BIAS = 1
+GEMM_EPI_BIAS_GELU = 2
+
 EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg", "attn_resolve_cfg",
-           "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows"]
+           "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows", "gemm_bf16"]
 
 
 class AttnError(RuntimeError):
@@ -112,6 +116,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.softmax_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p]
     lib.softmax_rows.restype = ctypes.c_int
+    lib.gemm_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gemm_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -270,3 +277,32 @@ def softmax(x, stream=None):
     y = torch.empty_like(x)
     softmax_rows(x, y, x.shape[0], x.shape[1], _softmax_dtype(x), stream)
     return y
+
+
+def gemm_bf16(a, w, bias, c, M, N, K, epilogue=GEMM_EPI_BIAS_GELU, stream=None) -> None:
+    """Enqueue C = epilogue(A W^T + bias) (see include/gemm.h); bias may be None with GEMM_EPI_NONE."""
+    lib = load_library()
+    _check(lib.gemm_bf16(_ptr(a), _ptr(w), _ptr(bias) if bias is not None else None, _ptr(c), int(M), int(N),
+                         int(K), int(epilogue), _stream_handle(stream, a)))
+
+
+def gemm(a, w, bias=None, epilogue=None, stream=None):
+    """GELU(a @ w.T + bias) (or the epilogue given) for contiguous bf16 a [M, K], w [N, K] and fp32
+    bias [N] on the GPU; returns a new bf16 [M, N] tensor."""
+    import torch
+
+    if epilogue is None:
+        epilogue = GEMM_EPI_NONE if bias is None else GEMM_EPI_BIAS_GELU
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError("a must be [M, K] and w [N, K]")
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("a and w must be bfloat16")
+    if not (a.is_contiguous() and w.is_contiguous()):
+        raise ValueError("a and w must be contiguous")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (w.shape[0],) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [N] tensor")
+    M, K = a.shape
+    N = w.shape[0]
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    gemm_bf16(a, w, bias, c, M, N, K, epilogue, stream)
+    return c

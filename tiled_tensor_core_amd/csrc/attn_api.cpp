@@ -8,8 +8,10 @@
 #include <string>
 
 #include "../../include/attn.h"
+#include "../../include/gemm.h"
 #include "../../include/softmax.h"
 #include "attn_launch.h"
+#include "gemm_launch.h"
 #include "softmax_launch.h"
 
 namespace {
@@ -118,9 +120,42 @@ int run_softmax(const void* x, void* y, int rows, int cols, int dtype, void* str
   return ATTN_OK;
 }
 
+int run_gemm(const void* a, const void* w, const float* bias, void* c, int M, int N, int K, int epi,
+             void* stream) {
+  if (epi != GEMM_EPI_NONE && epi != GEMM_EPI_BIAS && epi != GEMM_EPI_BIAS_GELU) return ATTN_ERR_CONFIG;
+  if (!a || !w || !c || (epi != GEMM_EPI_NONE && !bias)) return ATTN_ERR_NULL;
+  constexpr int kMaxNK = 4194296;   // 256 rows of N or K bf16 values within 2^31 bytes
+  if (M < 1 || N < 8 || K < 8 || N % 8 != 0 || K % 8 != 0 || N > kMaxNK || K > kMaxNK)
+    return ATTN_ERR_SHAPE;
+  if (misaligned(a) || misaligned(w) || misaligned(c) || (bias && misaligned(bias))) return ATTN_ERR_ALIGN;
+  const size_t a_bytes = (size_t)M * K * 2, w_bytes = (size_t)N * K * 2, c_bytes = (size_t)M * N * 2;
+  if (overlaps(c, c_bytes, a, a_bytes) || overlaps(c, c_bytes, w, w_bytes) ||
+      (bias && overlaps(c, c_bytes, bias, (size_t)N * 4)))
+    return ATTN_ERR_ALIAS;
+  ttc_gemm::GemmParams prm{};
+  prm.a = static_cast<const uint16_t*>(a);
+  prm.w = static_cast<const uint16_t*>(w);
+  prm.bias = bias;
+  prm.c = static_cast<uint16_t*>(c);
+  prm.M = M;
+  prm.N = N;
+  prm.K = K;
+  hipError_t e = ttc_gemm::launch_gemm(epi, prm, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_bf16(const void* a, const void* w, const float* bias, void* c, int M, int N, int K, int epilogue,
+              void* stream) {
+  return run_gemm(a, w, bias, c, M, N, K, epilogue, stream);
+}
 
 int softmax_rows(const void* x, void* y, int rows, int cols, int dtype, void* stream) {
   return run_softmax(x, y, rows, cols, dtype, stream);

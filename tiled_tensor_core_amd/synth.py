@@ -29,7 +29,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "x": 3}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "x": 3, "a": 4, "w": 5, "bias": 6}
 
 
 @dataclass(frozen=True)
@@ -211,3 +211,43 @@ def softmax_to_torch(x: np.ndarray, dtype: str, device="cpu"):
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
         return t.to(device) if device != "cpu" else t
     return to_torch(x, dtype, device)
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    """C = GELU(A W^T + b): A [M, K] ~ N(0, 1), W [N, K] ~ N(0, 1/K) (the
+    scale of a linear layer's initialisation, so A W^T is of order 1 and
+    GELU sees both signs), b [N] ~ U(-1, 1), A and W rounded to bf16."""
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int = 0
+
+    def describe(self) -> str:
+        return f"M={self.M},N={self.N},K={self.K},bf16"
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+GEMM_WORKLOADS = {
+    # the up-projection of a transformer MLP for the attention workload's tokens:
+    # 8 x 2048 tokens, hidden 4096 (32 heads of 128), 4x expansion
+    "mlp": GemmWorkload("mlp", 16384, 16384, 4096),
+    # ragged in every dimension: several tiles, partial tiles, a K tail
+    "ragged": GemmWorkload("ragged", 1000, 776, 328),
+    "small": GemmWorkload("small", 300, 264, 200),
+}
+
+
+def make_gemm_inputs(M: int, N: int, K: int, seed: int = 0):
+    """A, W as uint16 bf16 bits and the fp32 bias, for C = GELU(A W^T + b)."""
+    a = round_bits(draw(N01, M * K, seed, TENSOR_IDS["a"]).reshape(M, K), "bf16")
+    w = round_bits(draw(Dist("normal", float(K) ** -0.5), N * K, seed, TENSOR_IDS["w"]).reshape(N, K), "bf16")
+    b = draw(Dist("uniform", 1.0), N, seed, TENSOR_IDS["bias"]).astype(np.float32)
+    return a, w, b
+
+
+def make_gemm_workload(w: GemmWorkload):
+    return make_gemm_inputs(w.M, w.N, w.K, w.seed)
