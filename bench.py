@@ -125,6 +125,7 @@ def time_launches(torch, launch, stream, steps, warmup, warmup_s=WARMUP_MIN_S):
         "kernel_ms_mean": float(np.mean(per)),
         "kernel_ms_median": float(np.median(per)),
         "kernel_ms_min": float(per[0]),
+        "kernel_ms_p90": float(np.percentile(per, 90)),
     }
 
 
@@ -254,6 +255,8 @@ def run_softmax(a, torch, attn, synth):
             "traffic": traffic,
             "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
             "kernel_ms_median": round(r["kernel_ms_median"], 5),
+            "kernel_ms_min": round(r["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(r["kernel_ms_p90"], 5),
         },
     }
     if a.extra:
@@ -358,6 +361,8 @@ def run_gemm(a, torch, attn, synth):
             "traffic": traffic,
             "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
             "kernel_ms_median": round(r["kernel_ms_median"], 5),
+            "kernel_ms_min": round(r["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(r["kernel_ms_p90"], 5),
         },
     }
     if a.extra:
@@ -493,6 +498,8 @@ def main():
             "traffic": traffic,
             "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
             "kernel_ms_median": round(r["kernel_ms_median"], 5),
+            "kernel_ms_min": round(r["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(r["kernel_ms_p90"], 5),
         },
     }
     if a.extra:

@@ -356,16 +356,13 @@ __global__ void __launch_bounds__(kWaves * 64) softmax_elem(const uint8_t* x, ui
   }
 }
 
+// Compute units of the current device (the runtime caches the attribute).
 static int cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cus = n > 0 ? n : 256;
-    else
-      cus = 256;
-  }
-  return cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    return n;
+  return 256;
 }
 
 // Wave-per-row paths: as many workgroups of kWaves waves as the device keeps
