@@ -72,9 +72,13 @@ def test_every_candidate_is_bit_identical(B, H, N, d, dtype, causal):
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")
 def test_resolved_builtin_configuration():
+    # 4096 items, at least 4 per resident workgroup: one domain, twice the resident grid, groups of 8
     c = attn.attn_resolve_cfg(8, 32, 2048, 128, 1, attn.ATTN_BF16)
-    items_per_dom = 8 * 32 * 16 // c.n_dom
-    assert c.n_dom == 8 and 1 <= c.n_work <= items_per_dom and c.grp >= 1 and c.prio == attn.ATTN_PRIO_ON
+    assert c.n_dom == 1 and c.grp == 8 and c.prio == attn.ATTN_PRIO_ON and 2 <= c.n_work <= 8 * 32 * 16
+    # 512 items, one per resident workgroup on this device: 8 domains, the resident grid
+    cm = attn.attn_resolve_cfg(4, 16, 1024, 64, 1, attn.ATTN_BF16)
+    assert cm.n_dom == 8 and 1 <= cm.n_work <= 4 * 16 * 8 // 8 and cm.grp >= 1
+    assert c.n_work >= 2 * cm.n_work * cm.n_dom or c.n_work == 8 * 32 * 16
     c1 = attn.attn_resolve_cfg(1, 3, 500, 64, 0, attn.ATTN_FP16)
     assert c1.n_dom == 1 and c1.n_work <= 3 * 4 and c1.grp <= 3
     # explicit fields are kept, within what the shape allows
