@@ -16,8 +16,9 @@
 //   * K advances 64 at a time.  A [256 x 64] and W [256 x 64] slices go
 //     from HBM straight into LDS with buffer_load_dwordx4 ... lds (16 bytes
 //     per lane, 1 KiB per wave instruction), double-buffered: the loads of
-//     slice j+1 are in flight while the MFMAs consume slice j, interleaved
-//     with the MFMAs of its first half together with the fragment reads.
+//     slice j+1 are issued in the last k16 step of slice j-1 and land while
+//     the MFMAs consume slice j; that last step also reads slice j's first
+//     fragments, so no slice starts by waiting for LDS.
 //     The two buffers are distinct LDS objects and the loop is unrolled by
 //     two, so the compiler can tell the DMA target from the buffer being
 //     read.
@@ -158,15 +159,6 @@ gemm_kernel(GemmParams p) {
     ld_row[s] = row;
     ld_k[s] = 8 * ((idx & 7) ^ ((row >> 1) & 7));
   }
-  auto load_half = [&](lds_u8* abuf, lds_u8* wbuf, int k0, int half) {
-#pragma unroll
-    for (int s = 4 * half; s < 4 * half + 4; ++s) {
-      const int k = k0 + ld_k[s];
-      const uint32_t off = k < K ? (uint32_t)(ld_row[s] * K + k) * 2u : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(abuf + (wave * kLoadsPerWave + s) * 1024), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void*)(wbuf + (wave * kLoadsPerWave + s) * 1024), 16, off, 0, 0, 0);
-    }
-  };
   auto load_slice = [&](lds_u8* abuf, lds_u8* wbuf, int k0) {
 #pragma unroll
     for (int s = 0; s < kLoadsPerWave; ++s) {
@@ -216,59 +208,86 @@ gemm_kernel(GemmParams p) {
     }
   }
 
-  // Fragment reads run one k16 step ahead of the MFMAs that use them (two
-  // register sets), and the next slice's loads go out in the first two
-  // steps.  Scheduling group barriers interleave them with the MFMAs: one
-  // fragment read (and, in the first two steps, one load) between every
-  // two MFMAs.  LDS is the busiest unit here -- the loads write 64 KiB and
-  // the fragment reads read 128 KiB per slice per compute unit -- and a
-  // burst of reads from all four waves queued behind the load traffic
-  // stalled the matrix cores; spread out, the same work ran 3-8 % faster.
-  // A scheduling barrier closes each step, so no read moves up into an
-  // earlier step.
+  // Fragment reads run one k16 step ahead of the MFMAs that use them, and
+  // scheduling group barriers interleave them with the MFMAs, one read
+  // between every two MFMAs.  LDS is the busiest unit here -- the loads
+  // write 64 KiB and the fragment reads read 128 KiB per slice per compute
+  // unit -- and a burst of reads from all four waves queued behind the load
+  // traffic stalled the matrix cores; spread out, the same work ran 3-8 %
+  // faster.  A scheduling barrier closes each step, so no read moves up
+  // into an earlier step.
   auto read_frags = [&](const lds_u8* abuf, const lds_u8* wbuf, int kk, u32x4 (&af)[4], u32x4 (&wf)[4]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read16(abuf + a_base + mb * 32 * kRowBytes + rd[kk]);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) wf[nb] = lds_read16(wbuf + w_base + nb * 32 * kRowBytes + rd[kk]);
   };
-  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, lds_u8* nabuf, lds_u8* nwbuf, int nk0, bool ld) {
-    u32x4 af[2][4], wf[2][4];
-    read_frags(abuf, wbuf, 0, af[0], wf[0]);
-    __builtin_amdgcn_sched_barrier(0);
+  // The first k16 step of a slice reads its fragments during the last step
+  // of the slice before: that step waits for the next slice's loads and
+  // holds the barrier after its first four MFMAs, then reads the next
+  // slice's first fragments and issues the loads of the slice after it
+  // (into the buffer just read) between its remaining MFMAs.  So no slice
+  // starts by waiting for LDS.  Two fragment register sets alternate:
+  // A (af0/wf0) for steps 0 and 2, B for steps 1 and 3.
+  u32x4 af0[4], wf0[4];
+  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, const lds_u8* nabuf, const lds_u8* nwbuf,
+                     lds_u8* dabuf, lds_u8* dwbuf, int dk0) {
+    u32x4 af1[4], wf1[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) read_frags(abuf, wbuf, kk + 1, af[(kk + 1) & 1], wf[(kk + 1) & 1]);
-      if (kk < 2 && ld) load_half(nabuf, nwbuf, nk0, kk);
+    for (int kk = 0; kk < 3; ++kk) {
+      if (kk & 1)
+        read_frags(abuf, wbuf, kk + 1, af0, wf0);
+      else
+        read_frags(abuf, wbuf, kk + 1, af1, wf1);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(wf[kk & 1][nb], af[kk & 1][mb], acc[mb][nb]);
-      // one fragment read (and one load in the first two steps) between every two MFMAs
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = (kk & 1) ? mfma(wf1[nb], af1[mb], acc[mb][nb]) : mfma(wf0[nb], af0[mb], acc[mb][nb]);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        if (kk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (kk < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // step 3
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[0][nb] = mfma(wf1[nb], af1[0], acc[0][nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(nabuf, nwbuf, 0, af0, wf0);
+    load_slice(dabuf, dwbuf, dk0);
+#pragma unroll
+    for (int mb = 1; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(wf1[nb], af1[mb], acc[mb][nb]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- main loop: two slices per iteration, one per buffer --------------------
   // The slice count is rounded up to even (a slice past K reads as zeros),
   // so the loop has one exit and the accumulators one loop-carried copy.
+  // The last two slices issue loads past K, which only write zeros into
+  // LDS; the barrier after the loop waits for them.
   const int nk = ((K + kBK - 1) / kBK + 1) & ~1;
   load_slice(A0, W0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  load_slice(A1, W1, kBK);
+  read_frags(A0, W0, 0, af0, wf0);
   for (int j = 0; j < nk; j += 2) {
-    // slice j in buffer 0
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute(A0, W0, A1, W1, (j + 1) * kBK, true);
-    // slice j + 1 in buffer 1
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute(A1, W1, A0, W0, (j + 2) * kBK, j + 2 < nk);
+    compute(A0, W0, A1, W1, A0, W0, (j + 2) * kBK);   // slice j; reads slice j+1, loads slice j+2
+    compute(A1, W1, A0, W0, A1, W1, (j + 3) * kBK);   // slice j+1; reads slice j+2, loads slice j+3
   }
   // every wave is done reading the slices: LDS is free for the output.  The
   // scheduling barriers keep the accumulator reads of the epilogue below
@@ -334,5 +353,6 @@ hipError_t launch_gemm(int epi, const GemmParams& prm, hipStream_t stream) {
 }
 
 }  // namespace ttc_gemm
+
 
 
