@@ -97,6 +97,32 @@ def test_peaky_rows(dtype):
         full_check(q, k, v, dtype, causal, 1 / np.sqrt(d), tag=f"peaky {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_dominant_key_below_the_rescale_margin(d):
+    """A key in the second tile outweighs the first tile's maximum by a factor
+    p = 2.0077 (under the bf16 kernel's 2^2 margin, so the reference maximum
+    stays at the first tile).  bf16 rounds that P to 2.0, 0.38 % low.  Keys 0
+    and 64 share one large value row (|v| up to 40), so the exact O is that
+    row.  If O were divided by the sum of the unrounded p, the rounding would
+    pull O 0.26 % towards 0, up to 0.1: ten times the tolerance."""
+    B, H, N = 1, 2, 256
+    q = np.zeros((B, H, N, d), dtype=np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((B, H, N, d), dtype=np.float32)
+    k[..., 0] = -32.0          # p = exp(-22.3) relative to key 0
+    k[:, :, 0, 0] = 0.0
+    k[:, :, 64, 0] = 1.0
+    scale = float(np.log(2.0) + np.log1p(0.98 * 2.0 ** -8))   # key 64: p = 2 (1 + 0.98 * 2^-8)
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    big = np.clip(16.0 * rng.standard_normal((B, H, d)), -40.0, 40.0).astype(np.float32)
+    v[:, :, 0] = big
+    v[:, :, 64] = big
+    qb, kb, vb = (synth.round_bits(x, "bf16") for x in (q, k, v))
+    for causal in (False, True):
+        full_check(qb, kb, vb, "bf16", causal, scale, tag=f"dominant key d={d} causal={causal}")
+
+
 def test_increasing_keys():
     """Scores that grow along the key axis: every tile raises the maximum."""
     B, H, N, d = 1, 1, 300, 64

@@ -54,11 +54,15 @@
 //   * the running maximum m used as the exponent reference moves (and O, l
 //     are rescaled by alpha = exp2((m_old - m_new)*c)) only when some row's
 //     tile maximum exceeds it by more than a margin (in log2 units); else
-//     alpha = 1.  bf16 uses a zero margin: m is the exact running maximum,
-//     so a row's largest probability is exactly 1 and survives the bf16
-//     rounding of P without error (this matters on peaky rows).  fp16, with
-//     3 more bits of mantissa for P, keeps a stale reference until a row
-//     outgrows it by 2^8 (p <= 256).  O / l and LSE do not depend on the
+//     alpha = 1, and the tile skips the 64 multiplies of O.  fp16 keeps a
+//     stale reference until a row outgrows it by 2^8 (p <= 256).  bf16 uses
+//     2^2 (p <= 4), and corrects for the rounding of P: on a peaky row one
+//     key carries nearly all the weight, and the bf16 rounding of its P (up
+//     to 2^-9 relative) would reach O in full, since l sums the unrounded p.
+//     So for each tile the wave adds bf16(p) - p of the row's largest score
+//     to a per-row term corr (rescaled with l), and O is divided by l + corr:
+//     the dominant key's weight is then the same in O's numerator and
+//     denominator.  LSE uses l alone.  O / l and LSE do not depend on the
 //     reference.
 //
 // LDS layout: K buffer 0, K buffer 1, V buffer 0, V buffer 1; each a [64][D]
@@ -212,6 +216,7 @@ struct Wave {
   f32x16 oacc[DT];   // O^T accumulator of the wave's 32 rows
   u32x4 pb[KB][2];   // 16-bit P^T fragments (B operand of O^T += V^T P^T)
   float m, l;        // running maximum (raw score units) and row sum
+  float corr;        // bf16: sum of bf16(p) - p of each tile's largest score (reference m)
   float c, thr;      // score multiplier |scale|*log2(e); margin before m moves
   float alpha;       // pending rescale factor of O and l for the current tile
   float mc;          // m * c, the exponent offset of the current tile
@@ -296,6 +301,10 @@ struct Wave {
     alpha = fast_exp2((m - mref) * c);  // 0 while m is -inf, 1 if m stays
     m = mnew;
     mc = mref * c;
+    if (BF16) {  // p of the tile's largest score, bit-identical to prob()'s
+      const float pm = fast_exp2(__builtin_fmaf(mx, c, -mc));
+      corr = __builtin_fmaf(corr, alpha, (float)(__bf16)pm - pm);
+    }
   }
   TTC_INLINE void max_all(f32x16 (&s)[KB]) {
     float mx = s[0][0];
@@ -682,6 +691,7 @@ attn_fwd_kernel(AttnParams p) {
     // ---- running state -------------------------------------------------------
     w.m = -INFINITY;
     w.l = 0.0f;
+    w.corr = 0.0f;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -809,7 +819,7 @@ attn_fwd_kernel(AttnParams p) {
       if (1 < n_tiles2) load_kv(krs2, koff, K1, 1);
       if (last_odd) load_kv(vrs2, voff, V0, 0);
     }
-    // ---- epilogue: O = acc / l, LSE = ln2 * (m*c + log2 l) -----------------
+    // ---- epilogue: O = acc / (l + corr), LSE = ln2 * (m*c + log2 l) ----------
     // A lane holds 4-float pieces of one row of O, so storing from the
     // accumulators writes 32 bytes into each of 32 rows per instruction.
     // Instead each wave turns every 32x32 block of O row-major in a private
@@ -818,7 +828,7 @@ attn_fwd_kernel(AttnParams p) {
     // whole 128-byte row pieces.
     auto epilogue = [&](lds_u8* stage) {
       const float lt = pair_sum(w.l);
-      const float inv = __builtin_amdgcn_rcpf(lt);
+      const float inv = __builtin_amdgcn_rcpf(BF16 ? lt + w.corr : lt);
       // lane-derived offsets computed here, not hoisted out of the item loop
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -946,9 +956,10 @@ hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const 
                            hipStream_t stream) {
   const int bm = block_rows(d);
   prm.n_qblk = (prm.N + bm - 1) / bm;
-  // raw-score margin before the reference maximum moves: 0 for bf16 (exact
-  // running maximum), 2^8 in probability units for fp16
-  prm.thr = bf16 ? 0.0f : fminf(8.0f / prm.c, 3.0e38f);
+  // raw-score margin before the reference maximum moves: 2^2 in probability
+  // units for bf16 (whose kernel corrects the rounding of each tile's largest
+  // P), 2^8 for fp16
+  prm.thr = fminf((bf16 ? 2.0f : 8.0f) / prm.c, 3.0e38f);
   const long long items = (long long)prm.BH * prm.n_qblk;
   if (items > (1LL << 30)) return hipErrorInvalidConfiguration;
   prm.n_dom = cfg.n_dom;
