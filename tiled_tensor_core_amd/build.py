@@ -71,15 +71,19 @@ def build(isa_dir: str | None = None, verbose: bool = False) -> str:
     # every kernel is designed to live in registers: scratch means spills or
     # a register array the compiler could not keep in registers
     kernel = None
+    spills = []
     for line in report:
         m = re.search(r"Function Name: (\S+)", line)
         if m:
             kernel = m.group(1)
         m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
         if m and int(m.group(1)) > 0:
-            print(f"warning: {kernel} uses {m.group(1)} bytes of scratch per lane", file=sys.stderr)
+            spills.append(f"{kernel}: {m.group(1)} bytes of scratch per lane")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels spill registers to scratch memory:\n  " + "\n  ".join(spills))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

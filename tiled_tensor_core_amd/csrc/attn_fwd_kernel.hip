@@ -270,12 +270,14 @@ struct Wave {
   // row; delta = 0: block 0 is the triangle, block 1 all future keys;
   // delta = -32: block 1 is the triangle.  In the triangle, key
   // 8*(r/4) + r%4 + 4*(lane/32) of the block is hidden from row lane%32 when
-  // it is larger; the lanes that hide score r form a constant mask.  Each
-  // score takes one v_cndmask on a mask the scalar unit selects.
+  // it is larger; the lanes that hide score r form a constant mask, and
+  // the score takes one v_cndmask on it.
   TTC_INLINE static unsigned long long tri_lanes(int r) { return kTriLanes.m[r]; }
   // Lanes that hide score r of 32-key block kb, whose first key is db =
   // delta + 32*kb keys after the wave's first row: all (db >= 32), the
-  // triangle (db = 0) or none (db <= -32).
+  // triangle (db = 0) or none (db <= -32).  Selected per score, this costs
+  // four scalar instructions a score (the d = 64 steps, short of registers
+  // for the branches of diag_mask8, use it).
   TTC_INLINE static unsigned long long diag_lanes(int delta, int kb, int r) {
     const int db = delta + 32 * kb;
     return db >= 32 ? ~0ull : (db == 0 ? tri_lanes(r) : 0ull);
@@ -284,9 +286,25 @@ struct Wave {
     const int kb = e >> 4, r = e & 15;
     s[kb][r] = __builtin_amdgcn_inverse_ballot_w64(diag_lanes(delta, kb, r)) ? -INFINITY : s[kb][r];
   }
+  // Scores e0 .. e0+7 (all in 32-key block kb = e0 / 16) under that mask:
+  // one uniform branch picks the block's case, so only a triangle block
+  // pays for its per-score lane masks (about 100 fewer scalar instructions
+  // per masked tile than diag_mask_one).
+  TTC_INLINE static void diag_mask8(f32x16 (&s)[KB], int delta, int e0) {
+    const int kb = e0 >> 4;
+    const int db = delta + 32 * kb;
+    if (db >= 32) {
+#pragma unroll
+      for (int e = e0; e < e0 + 8; ++e) s[kb][e & 15] = -INFINITY;
+    } else if (db == 0) {
+#pragma unroll
+      for (int e = e0; e < e0 + 8; ++e)
+        s[kb][e & 15] = __builtin_amdgcn_inverse_ballot_w64(tri_lanes(e & 15)) ? -INFINITY : s[kb][e & 15];
+    }
+  }
   TTC_INLINE static void diag_mask(f32x16 (&s)[KB], int delta) {
 #pragma unroll
-    for (int e = 0; e < NS; ++e) diag_mask_one(s, delta, e);
+    for (int e0 = 0; e0 < NS; e0 += 8) diag_mask8(s, delta, e0);
   }
   // The row's tile maximum mx (both lane halves) moves the reference
   // maximum if some row of the wave outgrew it by the margin (always on the
@@ -406,8 +424,12 @@ struct Wave {
         } else {
           const int t = cc / 4 + 1;
           if (MASKN && cc >= 8 && cc < 12) {
+            if constexpr (D == 128) {
+              diag_mask8(sn, mdelta, 8 * (cc - 8));
+            } else {   // (the branches cost the d = 64 step registers it does not have)
 #pragma unroll
-            for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
+              for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
+            }
           }
           if (RESCALE && t < DT) {
 #pragma unroll
@@ -456,15 +478,35 @@ struct Wave {
 // LDS at dst: PER_W buffer_load_dwordx4 ... lds, lane offsets off[] within
 // the tile.  Rows of the tile past N (only in the last tile) are clamped to
 // row N-1, keeping the swizzled slot of the row they stand in for.
-TTC_INLINE void load_one(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, int off, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, soff, 0, 0);
+//
+// The load is issued from inline assembly, so the compiler does not see it as
+// a write of LDS.  Seen as one, it makes every later LDS read that it cannot
+// prove to be in another buffer (a buffer chosen at run time, or one of more
+// distinct load sites than it tracks) wait until all loads in flight have
+// landed -- in the middle of a tile, a full memory round trip.  Every tile a
+// load fills is read only after the wait at the start of a later step
+// (vmcnt(0), then a workgroup barrier), so no other wait is needed.  The
+// buffer resource is a plain 4-dword descriptor in scalar registers; M0 holds
+// the LDS address, and one wait state separates its write from the load.
+TTC_INLINE void load_one(u32x4 rs, lds_u8* dst, int off, int soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
 }
 
 template <int PER_W, int ROW_BYTES, int BC>
-TTC_INLINE void load_tile(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, const int* off, int j) {
+TTC_INLINE void load_tile(u32x4 rs, lds_u8* dst, const int* off, int j) {
 #pragma unroll
-  for (int t = 0; t < PER_W; ++t)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + t * 1024), 16, off[t], j * BC * ROW_BYTES, 0, 0);
+  for (int t = 0; t < PER_W; ++t) load_one(rs, dst + t * 1024, off[t], j * BC * ROW_BYTES);
+}
+
+// The same descriptor as head_rsrc below, as four dwords: base address
+// (48 bits, stride 0), size in bytes, and the format word.
+TTC_INLINE u32x4 load_rsrc(const void* base, unsigned nbytes) {
+  const uint64_t a = (uint64_t)(size_t)base;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
 }
 
 // Buffer resource spanning nbytes from base (one head's K, V or O); loads
@@ -588,7 +630,7 @@ attn_fwd_kernel(AttnParams p) {
     return (min(r, N - 1 - j_tail * BC) - r) * ROW_BYTES;
   };
   const int wofs = wave * PER_W * 1024;   // this wave's share of a tile
-  auto load_kv = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[PER_W], lds_u8* buf, int j) {
+  auto load_kv = [&](u32x4 rs, const int (&off)[PER_W], lds_u8* buf, int j) {
     if (j == j_tail) {
       int o[PER_W];
 #pragma unroll
@@ -656,8 +698,8 @@ attn_fwd_kernel(AttnParams p) {
   };
   int t_item = 0, bh, qb;
   if (!item(0, bh, qb)) return;
-  __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + (size_t)bh * N * D, HEAD_BYTES);
-  __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + (size_t)bh * N * D, HEAD_BYTES);
+  u32x4 krs = load_rsrc(p.k + (size_t)bh * N * D, HEAD_BYTES);
+  u32x4 vrs = load_rsrc(p.v + (size_t)bh * N * D, HEAD_BYTES);
   int n_tiles = tiles_of(qb);
   load_q(bh, qb);
   load_kv(krs, koff, K0, 0);
@@ -761,7 +803,10 @@ attn_fwd_kernel(AttnParams p) {
     if (j < n_pipe) {
       wait_all();
       progress();
-      w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
+      if (w.moved)
+        w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
+      else
+        w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
       ++j;
@@ -792,10 +837,17 @@ attn_fwd_kernel(AttnParams p) {
       if constexpr (CAUSAL) {
         // a causal diagonal tile, masked in the pipeline (keys past N follow
         // every row below N, so the causal mask hides them as well)
-        w.template pipe_tile<true, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
-                                                                     (j + 1) * BC - wr0);
+        if (w.moved)
+          w.template pipe_tile<true, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
+                                                                       (j + 1) * BC - wr0);
+        else
+          w.template pipe_tile<false, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
+                                                                        (j + 1) * BC - wr0);
       } else {
-        w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
+        if (w.moved)
+          w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
+        else
+          w.template pipe_tile<false, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
         apply_mask(sb, j + 1);
         w.max_all(sb);
       }
@@ -810,8 +862,8 @@ attn_fwd_kernel(AttnParams p) {
     // now: start the next item's Q, K_0, K_1 and, when it is free, V_0.
     int bh2 = 0, qb2 = 0;
     const bool more = item(t_item + 1, bh2, qb2);
-    const __amdgpu_buffer_rsrc_t krs2 = head_rsrc(p.k + (size_t)bh2 * N * D, HEAD_BYTES);
-    const __amdgpu_buffer_rsrc_t vrs2 = head_rsrc(p.v + (size_t)bh2 * N * D, HEAD_BYTES);
+    const u32x4 krs2 = load_rsrc(p.k + (size_t)bh2 * N * D, HEAD_BYTES);
+    const u32x4 vrs2 = load_rsrc(p.v + (size_t)bh2 * N * D, HEAD_BYTES);
     const int n_tiles2 = tiles_of(qb2);
     const bool last_odd = j & 1;
     if (more) {
