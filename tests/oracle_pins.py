@@ -240,6 +240,98 @@ def run_all(impl):
     return failed
 
 
+# ---- pins of the probability matrix P (attention_probs) -------------------------
+# Each takes ``probs_fn(q, k, causal, scale) -> P [B, H, N, N]``.
+
+def probs_pin_golden(probs_fn):
+    """The hand-derived cases of tests/golden/closed_form_weights.json: with
+    q_i = [1, 0] and k_j = [ln w_j + shift, *] at scale 1, P_ij is the exact
+    fraction w_j / (sum of w over the keys row i sees)."""
+    with open(os.path.join(GOLDEN, "closed_form_weights.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        w = [Fraction(x) for x in c["w"]]
+        n = len(w)
+        q = np.tile(np.array([1.0, 0.0]), (n, 1))
+        k = np.stack([np.log(np.array(c["w"], dtype=np.float64)) + c["shift"],
+                      np.array(c["k_second"], dtype=np.float64)], axis=1)
+        p = probs_fn(q[None, None], k[None, None], c["causal"], 1.0)[0, 0]
+        want = np.zeros((n, n))
+        for i in range(n):
+            vis = range(i + 1) if c["causal"] else range(n)
+            tot = sum(w[j] for j in vis)
+            for j in vis:
+                want[i, j] = float(w[j] / tot)
+        assert np.max(np.abs(p - want)) <= 1e-13, c["name"]
+
+
+def probs_pin_log_ratio(probs_fn, N=7, d=5):
+    """Non-causal: ln P_ij - ln P_i0 = scale q_i . (k_j - k_0) exactly in real
+    arithmetic, whatever the normaliser; this fixes the scale, which operand
+    is the query, and that row i of P belongs to query i."""
+    q, k = _rand((1, 2, N, d), 37), _rand((1, 2, N, d), 38)
+    scale = 0.6
+    p = probs_fn(q, k, False, scale)
+    got = np.log(p) - np.log(p[..., :1])
+    want = scale * np.einsum("bhid,bhjd->bhij", q, k - k[:, :, :1])
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def probs_pin_high_precision(probs_fn, N=5, d=3):
+    """Every entry of P against a 50-digit evaluation, causal and not."""
+    import mpmath
+
+    mpmath.mp.dps = 50
+    q, k = _rand((1, 1, N, d), 39, 2.0), _rand((1, 1, N, d), 40, 2.0)
+    for causal in (False, True):
+        p = probs_fn(q, k, causal, 0.8)[0, 0]
+        for i in range(N):
+            vis = range(i + 1) if causal else range(N)
+            s = {j: mpmath.mpf(0.8) * mpmath.fsum(mpmath.mpf(q[0, 0, i, c]) * mpmath.mpf(k[0, 0, j, c])
+                                                  for c in range(d)) for j in vis}
+            z = mpmath.fsum(mpmath.exp(x) for x in s.values())
+            for j in range(N):
+                want = float(mpmath.exp(s[j]) / z) if j in s else 0.0
+                assert abs(p[i, j] - want) <= 1e-15, (causal, i, j)
+
+
+def probs_pin_times_v(probs_fn, N=11, d=4):
+    """P V and the row log-sum-exp reproduce the pinned one-shot oracle:
+    O = P V, and for every visible key ln P_ij = scale q_i . k_j - LSE_i."""
+    from oracle import attention_ref
+
+    q, k, v = _rand((2, 2, N, d), 41), _rand((2, 2, N, d), 42), _rand((2, 2, N, d), 43)
+    for causal in (False, True):
+        p = probs_fn(q, k, causal, 0.45)
+        o, lse = attention_ref(q, k, v, causal, 0.45)
+        assert np.max(np.abs(p @ v - o)) <= 1e-13
+        s = 0.45 * np.einsum("bhid,bhjd->bhij", q, k)
+        vis = ~np.triu(np.ones((N, N), dtype=bool), 1) if causal else np.ones((N, N), dtype=bool)
+        with np.errstate(divide="ignore"):
+            lp = np.log(p)
+        assert np.max(np.abs((lp - (s - lse[..., None]))[..., vis])) <= 1e-12
+
+
+PROBS_PINS = [
+    ("rows_sum_to_one", lambda f: softmax_rows_sum_to_one(f)),
+    ("golden", probs_pin_golden),
+    ("log_ratio", probs_pin_log_ratio),
+    ("high_precision", probs_pin_high_precision),
+    ("times_v", probs_pin_times_v),
+]
+
+
+def run_probs_pins(probs_fn):
+    failed = []
+    for name, pin in PROBS_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(probs_fn)
+        except (AssertionError, ValueError, FloatingPointError, IndexError, KeyError):
+            failed.append(name)
+    return failed
+
+
 def softmax_rows_sum_to_one(probs_fn, N=15, d=8):
     """Every row of P sums to 1 and masked entries are exactly 0."""
     q, k = _rand((2, 2, N, d), 35), _rand((2, 2, N, d), 36)

@@ -16,7 +16,7 @@ import pytest
 
 import oracle.attention as oa
 from oracle import attention_online, attention_probs, attention_ref, attention_rows
-from oracle_pins import ALL_PINS, run_all, softmax_rows_sum_to_one
+from oracle_pins import ALL_PINS, PROBS_PINS, run_all, run_probs_pins
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -41,8 +41,28 @@ def test_pin(impl, pin):
     fn(IMPLS[impl])
 
 
-def test_probability_rows_sum_to_one():
-    softmax_rows_sum_to_one(attention_probs)
+@pytest.mark.parametrize("pin", [name for name, _ in PROBS_PINS])
+def test_probs_pin(pin):
+    dict(PROBS_PINS)[pin](attention_probs)
+
+
+PROBS_MUTATIONS = [
+    ("scale dropped", "s = scale * (q[b, h] @ k[b, h].T)", "s = (q[b, h] @ k[b, h].T)"),
+    ("scale applied twice", "s = scale * (q[b, h] @ k[b, h].T)", "s = scale * scale * (q[b, h] @ k[b, h].T)"),
+    ("q and k swapped", "s = scale * (q[b, h] @ k[b, h].T)", "s = scale * (k[b, h] @ q[b, h].T)"),
+    ("mask keeps the future", "np.triu(np.ones((N, N), dtype=bool), 1)", "np.tril(np.ones((N, N), dtype=bool), -1)"),
+    ("mask hides the diagonal", "np.triu(np.ones((N, N), dtype=bool), 1)", "np.triu(np.ones((N, N), dtype=bool), 0)"),
+    ("normalised over the wrong axis", "p[b, h] = e / e.sum(axis=1, keepdims=True)",
+     "p[b, h] = e / e.sum(axis=0, keepdims=True)"),
+    ("transposed", "p[b, h] = e / e.sum(axis=1, keepdims=True)", "p[b, h] = (e / e.sum(axis=1, keepdims=True)).T"),
+    ("base-2 exponent", "e = np.exp(s - m)", "e = np.exp2(s - m)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PROBS_MUTATIONS, ids=[m[0] for m in PROBS_MUTATIONS])
+def test_planted_mistake_in_probs_is_caught(name, old, new):
+    mod = _mutant(old, new)
+    assert run_probs_pins(mod.attention_probs), f"planted mistake '{name}' passed every probability pin"
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 17, 64])
