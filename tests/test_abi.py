@@ -146,7 +146,7 @@ def test_softmax_rejects_invalid_arguments(over, code):
 
 BAD_CFGS = [  # (n_dom, n_work, grp, prio)
     (2, 0, 0, 0), (-1, 0, 0, 0), (16, 0, 0, 0), (0, -1, 0, 0), (0, (1 << 20) + 1, 0, 0),
-    (0, 0, -3, 0), (0, 0, 0, 3), (0, 0, 0, -1),
+    (0, 0, -3, 0), (0, 0, 0, 3), (0, 0, 0, -1), (0, 0, 0, 0, 3), (0, 0, 0, 0, -1),
 ]
 
 
@@ -179,8 +179,9 @@ def test_resolve_cfg_rejects_null():
 
 
 def test_cfg_forms():
-    assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1)
-    assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0)
+    assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1, 0)
+    assert attn._cfg((8, 64, 4, 1, 2)).as_tuple() == (8, 64, 4, 1, 2)
+    assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0, 0)
     assert attn._cfg(None) is None
 
 
@@ -208,3 +209,93 @@ def test_gemm_bias_may_be_null_without_a_bias_epilogue():
     at a later check (here: misaligned c), never on the bias."""
     lib = attn.load_library()
     assert lib.gemm_bf16(GA, GW, None, GC + 4, 100, 64, 32, 0, None) == 4
+
+
+# ---- the size limit is the same for every entry point, and exact ---------------
+
+@pytest.mark.parametrize("d,n_max", [(128, (1 << 23) - 129), (64, (1 << 24) - 129)])
+def test_length_limit_is_exact(d, n_max):
+    """The longest N whose fp32 O head plus 128 rows, (N + 128) * d * 4 bytes,
+    fits unsigned 32-bit offsets passes the shape check (the call then stops
+    at the misaligned q, before any HIP call); one more is rejected by both
+    attn_fwd and attn_resolve_cfg."""
+    assert (n_max + 128) * d * 4 <= 0xFFFFFFFF < (n_max + 129) * d * 4
+    assert _call("attn_fwd", B=1, H=1, N=n_max, d=d, q=Q + 8) == 4
+    assert _call("attn_fwd", B=1, H=1, N=n_max + 1, d=d, q=Q + 8) == 2
+    lib = attn.load_library()
+    cfg = attn.LaunchCfg()
+    assert lib.attn_resolve_cfg(1, 1, n_max + 1, d, 0, 0, ctypes.byref(cfg)) == 2
+    assert lib.attn_resolve_cfg(1, 1, n_max, d, 0, 0, ctypes.byref(cfg)) != 2
+
+
+# ---- tensor arguments are checked before their addresses go to the C ABI --------
+
+def _cpu_args(B=1, H=2, N=8, d=64, dtype=None):
+    import torch
+
+    dtype = dtype or torch.bfloat16
+    q, k, v = (torch.zeros((B, H, N, d), dtype=dtype) for _ in range(3))
+    o = torch.zeros((B, H, N, d), dtype=torch.float32)
+    lse = torch.zeros((B, H, N), dtype=torch.float32)
+    return dict(q=q, k=k, v=v, o=o, lse=lse)
+
+
+def _bad_tensor_cases():
+    import torch
+
+    return [
+        ("o", lambda a: a["o"].to(torch.bfloat16), TypeError, "o must be float32"),
+        ("o", lambda a: a["o"].to(torch.float16), TypeError, "o must be float32"),
+        ("lse", lambda a: a["lse"].to(torch.float64), TypeError, "lse must be float32"),
+        ("k", lambda a: a["k"].to(torch.float16), TypeError, "share one dtype"),
+        ("q", lambda a: a["q"].to(torch.float32), TypeError, "bfloat16 or float16"),
+        ("o", lambda a: a["o"][..., :32], ValueError, "elements"),
+        ("lse", lambda a: a["lse"][:, :, :4], ValueError, "elements"),
+        ("v", lambda a: torch.zeros((1, 2, 9, 64), dtype=torch.bfloat16), ValueError, "elements"),
+        ("q", lambda a: a["q"].transpose(2, 3).contiguous().transpose(2, 3), ValueError, "contiguous"),
+        ("o", lambda a: a["o"].transpose(2, 3).contiguous().transpose(2, 3), ValueError, "contiguous"),
+    ]
+
+
+@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("entry", ["attn_fwd", "attn_fwd_cfg", "attn_fwd_bf16"])
+def test_binding_checks_tensors(case, entry):
+    name, mutate, exc, msg = _bad_tensor_cases()[case]
+    a = _cpu_args()
+    a[name] = mutate(a)
+    with pytest.raises(exc, match=msg):
+        getattr(attn, entry)(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 8, 64, 0, 0.125, stream=0)
+
+
+def test_binding_checks_entry_point_dtype_and_device():
+    import torch
+
+    a = _cpu_args(dtype=torch.float16)
+    with pytest.raises(TypeError, match="bfloat16 for this entry point"):
+        attn.attn_fwd_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 8, 64, 0, 0.125, stream=0)
+    # every property right but the device: CPU tensors are refused
+    with pytest.raises(ValueError, match="on a GPU"):
+        attn.attn_fwd_fp16(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 8, 64, 0, 0.125, stream=0)
+    with pytest.raises(ValueError, match="on a GPU"):
+        attn.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 8, 64, 0, 0.125, stream=0)
+
+
+def test_binding_checks_softmax_and_gemm_tensors():
+    import torch
+
+    x = torch.zeros((4, 10), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="y must be"):
+        attn.softmax_rows(x, torch.zeros((4, 10), dtype=torch.float32), 4, 10, stream=0)
+    with pytest.raises(ValueError, match="elements"):
+        attn.softmax_rows(x, torch.zeros((4, 9), dtype=torch.bfloat16), 4, 10, stream=0)
+    with pytest.raises(ValueError, match="on a GPU"):
+        attn.softmax_rows(x, torch.zeros((4, 10), dtype=torch.bfloat16), 4, 10, stream=0)
+    a = torch.zeros((16, 32), dtype=torch.bfloat16)
+    w = torch.zeros((24, 32), dtype=torch.bfloat16)
+    b = torch.zeros((24,), dtype=torch.float32)
+    with pytest.raises(TypeError, match="c must be"):
+        attn.gemm_bf16(a, w, b, torch.zeros((16, 24), dtype=torch.float32), 16, 24, 32, stream=0)
+    with pytest.raises(ValueError, match="elements"):
+        attn.gemm_bf16(a, w, b[:8], torch.zeros((16, 24), dtype=torch.bfloat16), 16, 24, 32, stream=0)
+    with pytest.raises(ValueError, match="on a GPU"):
+        attn.gemm_bf16(a, w, b, torch.zeros((16, 24), dtype=torch.bfloat16), 16, 24, 32, stream=0)

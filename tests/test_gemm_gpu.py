@@ -113,6 +113,10 @@ def test_rejects_bad_arguments_before_launch():
     with pytest.raises(attn.AttnError) as e:
         attn.gemm_bf16(a, w, None, c, 4, 8, 16, attn.GEMM_EPI_BIAS)
     assert e.value.code == 1
+    # K = 12 is no multiple of 8: tensors sized for it pass the binding's
+    # checks, and the C ABI rejects the shape
+    a12 = torch.zeros((4, 12), dtype=torch.bfloat16, device="cuda")
+    w12 = torch.zeros((8, 12), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(attn.AttnError) as e:
-        attn.gemm_bf16(a, w, None, c, 4, 8, 12, attn.GEMM_EPI_NONE)
+        attn.gemm_bf16(a12, w12, None, c, 4, 8, 12, attn.GEMM_EPI_NONE)
     assert e.value.code == 2

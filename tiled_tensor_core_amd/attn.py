@@ -53,6 +53,9 @@ STATUS = {
 ATTN_PRIO_DEFAULT = 0
 ATTN_PRIO_ON = 1
 ATTN_PRIO_OFF = 2
+ATTN_REF_DEFAULT = 0
+ATTN_REF_FIXED = 1
+ATTN_REF_RUNNING = 2
 ATTN_MAX_WORKGROUPS = 1 << 20
 
 
@@ -60,13 +63,14 @@ class LaunchCfg(ctypes.Structure):
     """attn_launch_cfg of include/attn.h (a field of 0 takes the built-in choice)."""
 
     _fields_ = [("n_dom", ctypes.c_int), ("n_work", ctypes.c_int), ("grp", ctypes.c_int),
-                ("prio", ctypes.c_int)]
+                ("prio", ctypes.c_int), ("mode", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.n_dom, self.n_work, self.grp, self.prio)
+        return (self.n_dom, self.n_work, self.grp, self.prio, self.mode)
 
     def __repr__(self):
-        return f"LaunchCfg(n_dom={self.n_dom}, n_work={self.n_work}, grp={self.grp}, prio={self.prio})"
+        return (f"LaunchCfg(n_dom={self.n_dom}, n_work={self.n_work}, grp={self.grp}, prio={self.prio}, "
+                f"mode={self.mode})")
 
 GEMM_EPI_NONE = 0
 GEMM_EPI_BIAS = 1
@@ -164,7 +168,57 @@ def _check(code: int) -> None:
         raise AttnError(code, detail)
 
 
-def _args(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
+def _is_tensor(x) -> bool:
+    return hasattr(x, "data_ptr") and hasattr(x, "dtype")
+
+
+def check_tensors(q, k, v, o, lse, B, H, N, d, dtype_code=None) -> None:
+    """Host-side checks of tensor arguments before their pointers go to the C ABI.
+
+    The C ABI sees only addresses and sizes, so it cannot tell a wrongly
+    typed or sized buffer from a right one.  When the arguments are torch
+    tensors this checks what it would otherwise trust: q, k, v are 16-bit
+    floats of one dtype (the one ``dtype_code`` names, if given) with
+    B*H*N*d elements each; o is fp32 with B*H*N*d elements and lse fp32 with
+    B*H*N; every tensor is contiguous (the kernel reads and writes them as
+    dense [B, H, N, d] / [B, H, N] arrays) and all sit on one GPU.  Raw int
+    addresses are passed through unchecked (the caller's contract).
+    """
+    args = {"q": q, "k": k, "v": v, "o": o, "lse": lse}
+    tensors = {n: x for n, x in args.items() if _is_tensor(x)}
+    if not tensors:
+        return
+    import torch
+
+    half = (torch.bfloat16, torch.float16)
+    want = {ATTN_BF16: torch.bfloat16, ATTN_FP16: torch.float16}.get(dtype_code)
+    in_dtypes = {tensors[n].dtype for n in ("q", "k", "v") if n in tensors}
+    for n in ("q", "k", "v"):
+        if n in tensors and tensors[n].dtype not in half:
+            raise TypeError(f"{n} must be bfloat16 or float16, got {tensors[n].dtype}")
+    if len(in_dtypes) > 1:
+        raise TypeError(f"q, k, v must share one dtype, got {sorted(map(str, in_dtypes))}")
+    if want is not None and in_dtypes and in_dtypes != {want}:
+        raise TypeError(f"q, k, v must be {want} for this entry point, got {in_dtypes.pop()}")
+    for n in ("o", "lse"):
+        if n in tensors and tensors[n].dtype != torch.float32:
+            raise TypeError(f"{n} must be float32, got {tensors[n].dtype}")
+    n_qkv = int(B) * int(H) * int(N) * int(d)
+    sizes = {"q": n_qkv, "k": n_qkv, "v": n_qkv, "o": n_qkv, "lse": int(B) * int(H) * int(N)}
+    for n, x in tensors.items():
+        if x.numel() != sizes[n]:
+            raise ValueError(f"{n} has {x.numel()} elements; B={B}, H={H}, N={N}, d={d} needs {sizes[n]}")
+        if not x.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    devices = {x.device for x in tensors.values()}
+    if any(dv.type != "cuda" for dv in devices):
+        raise ValueError(f"every tensor must be on a GPU, got {sorted(map(str, devices))}")
+    if len(devices) > 1:
+        raise ValueError(f"every tensor must be on one GPU, got {sorted(map(str, devices))}")
+
+
+def _args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype_code=None):
+    check_tensors(q, k, v, o, lse, B, H, N, d, dtype_code)
     return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
             int(causal), float(scale), _stream_handle(stream, q))
 
@@ -175,7 +229,7 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None
     if dtype is None and isinstance(q, int):
         raise TypeError("dtype is required when q is a raw address")
     code = _dtype_code(q, dtype)
-    _check(lib.attn_fwd(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream), code))
+    _check(lib.attn_fwd(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code), code))
 
 
 def _cfg(cfg) -> LaunchCfg | None:
@@ -193,7 +247,7 @@ def attn_fwd_cfg(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=
         raise TypeError("dtype is required when q is a raw address")
     code = _dtype_code(q, dtype)
     c = _cfg(cfg)
-    _check(lib.attn_fwd_cfg(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream), code,
+    _check(lib.attn_fwd_cfg(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code), code,
                             ctypes.byref(c) if c is not None else None))
 
 
@@ -208,12 +262,12 @@ def attn_resolve_cfg(B, H, N, d, causal, dtype, cfg=None) -> LaunchCfg:
 
 def attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
     lib = load_library()
-    _check(lib.attn_fwd_bf16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream)))
+    _check(lib.attn_fwd_bf16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_BF16)))
 
 
 def attn_fwd_fp16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
     lib = load_library()
-    _check(lib.attn_fwd_fp16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream)))
+    _check(lib.attn_fwd_fp16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_FP16)))
 
 
 def attn_status_str(code: int) -> str:
@@ -258,6 +312,24 @@ def _softmax_dtype(x):
     return codes[x.dtype]
 
 
+def _check_plain(named, device_of=None):
+    """Tensors among ``named`` ({name: (tensor or int, dtype or None, numel)})
+    must have that dtype and element count, be contiguous and share one GPU."""
+    tensors = {n: spec for n, spec in named.items() if _is_tensor(spec[0])}
+    for n, (x, dt, numel) in tensors.items():
+        if dt is not None and x.dtype != dt:
+            raise TypeError(f"{n} must be {dt}, got {x.dtype}")
+        if x.numel() != numel:
+            raise ValueError(f"{n} has {x.numel()} elements, the sizes given need {numel}")
+        if not x.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    devices = {spec[0].device for spec in tensors.values()}
+    if any(dv.type != "cuda" for dv in devices):
+        raise ValueError(f"every tensor must be on a GPU, got {sorted(map(str, devices))}")
+    if len(devices) > 1:
+        raise ValueError(f"every tensor must be on one GPU, got {sorted(map(str, devices))}")
+
+
 def softmax_rows(x, y, rows, cols, dtype=None, stream=None) -> None:
     """Enqueue the row-wise softmax of [rows, cols] x into y (see include/softmax.h)."""
     lib = load_library()
@@ -265,6 +337,12 @@ def softmax_rows(x, y, rows, cols, dtype=None, stream=None) -> None:
         if isinstance(x, int):
             raise TypeError("dtype is required when x is a raw address")
         dtype = _softmax_dtype(x)
+    if _is_tensor(x) or _is_tensor(y):
+        import torch
+
+        want = {SOFTMAX_F32: torch.float32, SOFTMAX_BF16: torch.bfloat16, SOFTMAX_FP16: torch.float16}.get(int(dtype))
+        n = int(rows) * int(cols)
+        _check_plain({"x": (x, want, n), "y": (y, want, n)})
     _check(lib.softmax_rows(_ptr(x), _ptr(y), int(rows), int(cols), int(dtype), _stream_handle(stream, x)))
 
 
@@ -282,6 +360,12 @@ def softmax(x, stream=None):
 def gemm_bf16(a, w, bias, c, M, N, K, epilogue=GEMM_EPI_BIAS_GELU, stream=None) -> None:
     """Enqueue C = epilogue(A W^T + bias) (see include/gemm.h); bias may be None with GEMM_EPI_NONE."""
     lib = load_library()
+    if any(_is_tensor(x) for x in (a, w, bias, c)):
+        import torch
+
+        M_, N_, K_ = int(M), int(N), int(K)
+        _check_plain({"a": (a, torch.bfloat16, M_ * K_), "w": (w, torch.bfloat16, N_ * K_),
+                      "bias": (bias, torch.float32, N_), "c": (c, torch.bfloat16, M_ * N_)})
     _check(lib.gemm_bf16(_ptr(a), _ptr(w), _ptr(bias) if bias is not None else None, _ptr(c), int(M), int(N),
                          int(K), int(epilogue), _stream_handle(stream, a)))
 

@@ -25,6 +25,18 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Sizes the kernel can address.  B*H must fit an int; element offsets
+// between heads are 64-bit inside the kernel.  Within a head, K, V and O are
+// addressed with unsigned 32-bit byte offsets: O is fp32, and the stores of a
+// ragged last block of 128 rows compute offsets up to (N + 128) * d * 4.
+bool shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return false;
+  const long long bh = (long long)B * H;
+  const long long rows = bh * N;
+  if (bh > (1LL << 30) || rows > (1LL << 40) || rows * d > (1LL << 46)) return false;
+  return (long long)(N + 128) * d * 4 <= 0xffffffffLL;
+}
+
 // Fields of a caller's launch configuration: 0 (built-in choice) or in range.
 bool cfg_valid(const attn_launch_cfg* c, long long bh) {
   if (!c) return true;
@@ -33,6 +45,7 @@ bool cfg_valid(const attn_launch_cfg* c, long long bh) {
   if (c->n_work < 0 || c->n_work > ATTN_MAX_WORKGROUPS) return false;
   if (c->grp < 0) return false;
   if (c->prio != ATTN_PRIO_DEFAULT && c->prio != ATTN_PRIO_ON && c->prio != ATTN_PRIO_OFF) return false;
+  if (c->mode != ATTN_REF_DEFAULT && c->mode != ATTN_REF_FIXED && c->mode != ATTN_REF_RUNNING) return false;
   return true;
 }
 
@@ -44,13 +57,9 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
   if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-  // B*H must fit an int; element offsets are 64-bit inside the kernel.
+  if (!shape_ok(B, H, N, d)) return ATTN_ERR_SHAPE;
   const long long bh = (long long)B * H;
   const long long rows = bh * N;
-  if (bh > (1LL << 30) || rows > (1LL << 40) || rows * d > (1LL << 46)) return ATTN_ERR_SHAPE;
-  // one head's K, V or O is addressed with 32-bit byte offsets (O: fp32,
-  // with room for the rows of a ragged last block of 128)
-  if ((long long)(N + 128) * d * 4 > 0xffffffffLL) return ATTN_ERR_SHAPE;
   if (!cfg_valid(user_cfg, bh)) return ATTN_ERR_CONFIG;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return ATTN_ERR_ALIGN;
@@ -91,7 +100,7 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   }
 
   ttc::LaunchCfg cfg{};
-  if (user_cfg) cfg = {user_cfg->n_dom, user_cfg->n_work, user_cfg->grp, user_cfg->prio};
+  if (user_cfg) cfg = {user_cfg->n_dom, user_cfg->n_work, user_cfg->grp, user_cfg->prio, user_cfg->mode};
   hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, cfg);
   if (e == hipSuccess)
     e = ttc::launch_attn_fwd(dtype == ATTN_BF16, d, causal == 1, prm, cfg, static_cast<hipStream_t>(stream));
@@ -188,13 +197,13 @@ int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_lau
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
   if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+  if (!shape_ok(B, H, N, d)) return ATTN_ERR_SHAPE;
   const long long bh = (long long)B * H;
-  if (bh > (1LL << 30) || bh * N > (1LL << 40)) return ATTN_ERR_SHAPE;
   if (!cfg_valid(cfg, bh)) return ATTN_ERR_CONFIG;
   ttc::AttnParams prm{};
   prm.BH = (int)bh;
   prm.N = N;
-  ttc::LaunchCfg c{cfg->n_dom, cfg->n_work, cfg->grp, cfg->prio};
+  ttc::LaunchCfg c{cfg->n_dom, cfg->n_work, cfg->grp, cfg->prio, cfg->mode};
   const hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, c);
   if (e != hipSuccess) {
     g_last_error = hipGetErrorString(e);
@@ -204,6 +213,7 @@ int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_lau
   cfg->n_work = c.n_work;
   cfg->grp = c.grp;
   cfg->prio = c.prio;
+  cfg->mode = c.mode;
   return ATTN_OK;
 }
 
