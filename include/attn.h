@@ -105,18 +105,41 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
  *           is behind on its item list, so the two workgroups sharing a
  *           compute unit finish together; ATTN_PRIO_OFF: constant priority.
  *
+ *   mode    the exponent reference of the online softmax (attn_ref_mode
+ *           below).
+ *
  * A field of 0 (ATTN_PRIO_DEFAULT for prio) takes the built-in choice.  The
- * configuration changes only which workgroup computes which (head, query
- * block) item and in what order, never an item's arithmetic: every valid
- * configuration gives bit-identical o and lse. */
+ * fields other than mode change only which workgroup computes which (head,
+ * query block) item and in what order, never an item's arithmetic: every
+ * valid configuration of one mode gives bit-identical o and lse. */
 #define ATTN_MAX_WORKGROUPS (1 << 20)
 enum attn_prio { ATTN_PRIO_DEFAULT = 0, ATTN_PRIO_ON = 1, ATTN_PRIO_OFF = 2 };
+
+/* Exponent reference of the online softmax (the `mode` field).  Both modes
+ * divide O by the sum of the 16-bit probabilities that multiply V, so O is
+ * a weighted mean of the rows of V whatever the reference, and LSE uses the
+ * sum of the unrounded fp32 probabilities.  The modes differ only in
+ * rounding, within the same accuracy.
+ *   ATTN_REF_FIXED    each (head, 128-row block) takes the maximum score of
+ *                     each row over its first 64-key tile, raised by 48
+ *                     (bf16) or 4 (fp16) in log2 units, as that row's
+ *                     reference for all its tiles: no per-tile maximum, no
+ *                     rescale of O.  A block in which a sum of 16-bit
+ *                     probabilities passes 2^48 (bf16) or overflows (fp16),
+ *                     or turns NaN, is computed again within the same launch
+ *                     with each row's exact maximum (found by a pass over the
+ *                     block's keys) as its reference.  The built-in choice.
+ *   ATTN_REF_RUNNING  the reference follows the running maximum of every
+ *                     32-row wave, moved (and O rescaled) only when a row
+ *                     outgrows it by 2^2 (bf16) or 2^8 (fp16). */
+enum attn_ref_mode { ATTN_REF_DEFAULT = 0, ATTN_REF_FIXED = 1, ATTN_REF_RUNNING = 2 };
 
 typedef struct attn_launch_cfg {
   int n_dom;
   int n_work;
   int grp;
   int prio;
+  int mode;   /* attn_ref_mode */
 } attn_launch_cfg;
 
 /* attn_fwd with an explicit launch configuration; cfg NULL is attn_fwd.

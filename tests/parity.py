@@ -28,8 +28,9 @@ def gpu_available() -> bool:
         return False
 
 
-def run_hip(qb, kb, vb, dtype, causal, scale, stream=None, entry="attn_fwd"):
-    """Run the HIP path on storage bits; returns (O, LSE) as torch tensors on the GPU."""
+def run_hip(qb, kb, vb, dtype, causal, scale, stream=None, entry="attn_fwd", cfg=None):
+    """Run the HIP path on storage bits; returns (O, LSE) as torch tensors on the GPU.
+    ``cfg``: a launch configuration for attn_fwd_cfg (a tuple, dict or LaunchCfg)."""
     import torch
 
     from tiled_tensor_core_amd import attn
@@ -40,8 +41,11 @@ def run_hip(qb, kb, vb, dtype, causal, scale, stream=None, entry="attn_fwd"):
     B, H, N, d = q.shape
     o = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
-    fn = getattr(attn, entry)
-    fn(q, k, v, o, lse, B, H, N, d, int(causal), scale, stream)
+    if cfg is not None:
+        attn.attn_fwd_cfg(q, k, v, o, lse, B, H, N, d, int(causal), scale, stream, cfg=cfg)
+    else:
+        fn = getattr(attn, entry)
+        fn(q, k, v, o, lse, B, H, N, d, int(causal), scale, stream)
     torch.cuda.synchronize()
     return o, lse
 
@@ -68,9 +72,9 @@ def assert_close(o, lse, o_ref, lse_ref, tag=""):
     return m
 
 
-def full_check(qb, kb, vb, dtype, causal, scale, tag=""):
+def full_check(qb, kb, vb, dtype, causal, scale, tag="", cfg=None):
     """Whole-tensor comparison against the one-shot oracle."""
-    o, lse = run_hip(qb, kb, vb, dtype, causal, scale)
+    o, lse = run_hip(qb, kb, vb, dtype, causal, scale, cfg=cfg)
     o_ref, lse_ref = attention_ref(synth.bits_to_f64(qb, dtype), synth.bits_to_f64(kb, dtype),
                                    synth.bits_to_f64(vb, dtype), causal, scale)
     return assert_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, tag)
@@ -101,3 +105,32 @@ def sampled_check(qb, kb, vb, dtype, causal, scale, o, lse, full_heads, rows_per
         ref_o.append(ro); ref_l.append(rl)
     return assert_close(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o),
                         np.concatenate(ref_l), tag)
+
+
+def whole_check(qb, kb, vb, dtype, causal, scale, o, lse, tag=""):
+    """Compare whole GPU outputs (numpy) with the one-shot oracle, one head at
+    a time (bounded memory); the metrics are taken over the whole tensor."""
+    B, H, N, d = qb.shape
+    sq_diff = 0.0
+    sq_ref = 0.0
+    o_max = 0.0
+    l_max = 0.0
+    finite = bool(np.all(np.isfinite(o)) and np.all(np.isfinite(lse)))
+    for b in range(B):
+        for h in range(H):
+            ro, rl = attention_ref(synth.bits_to_f64(qb[b, h][None, None], dtype),
+                                   synth.bits_to_f64(kb[b, h][None, None], dtype),
+                                   synth.bits_to_f64(vb[b, h][None, None], dtype), causal, scale)
+            diff = o[b, h].astype(np.float64) - ro[0, 0]
+            sq_diff += float(np.sum(diff * diff))
+            sq_ref += float(np.sum(ro * ro))
+            o_max = max(o_max, float(np.max(np.abs(diff))))
+            l_max = max(l_max, float(np.max(np.abs(lse[b, h].astype(np.float64) - rl[0, 0]))))
+    m = {"o_max_abs": o_max, "o_rel_fro": float(np.sqrt(sq_diff / max(sq_ref, 1e-300))),
+         "lse_max_abs": l_max, "finite": finite, "rows": B * H * N}
+    print(f"[parity] {tag} {m}", flush=True)
+    assert m["finite"], f"{tag}: non-finite output {m}"
+    assert m["o_max_abs"] <= O_MAX_ABS, f"{tag}: O max-abs {m}"
+    assert m["o_rel_fro"] <= O_REL_FRO, f"{tag}: O rel-Frobenius {m}"
+    assert m["lse_max_abs"] <= LSE_MAX_ABS, f"{tag}: LSE max-abs {m}"
+    return m

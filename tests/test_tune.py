@@ -25,8 +25,8 @@ def test_cache_roundtrip(tmp_path):
     data = json.load(open(path))
     assert set(data) == {key, "fp16/d64/full/BH12/N100"}
     assert "first_pass" not in data[key]
-    assert tune.lookup("bf16", 128, True, 256, 2048, path).as_tuple() == (8, 64, 4, 1)
-    assert tune.lookup("fp16", 64, False, 12, 100, path).as_tuple() == (1, 5, 2, 2)
+    assert tune.lookup("bf16", 128, True, 256, 2048, path).as_tuple() == (8, 64, 4, 1, 0)
+    assert tune.lookup("fp16", 64, False, 12, 100, path).as_tuple() == (1, 5, 2, 2, 0)
     assert tune.lookup("fp16", 64, True, 12, 100, path) is None
 
 
@@ -83,7 +83,7 @@ def test_resolved_builtin_configuration():
     assert c1.n_dom == 1 and c1.n_work <= 3 * 4 and c1.grp <= 3
     # explicit fields are kept, within what the shape allows
     c2 = attn.attn_resolve_cfg(8, 32, 2048, 128, 1, attn.ATTN_BF16, attn.LaunchCfg(1, 10 ** 6, 1000, 2))
-    assert c2.as_tuple() == (1, 8 * 32 * 16, 8 * 32, 2)
+    assert c2.as_tuple() == (1, 8 * 32 * 16, 8 * 32, 2, attn.ATTN_REF_FIXED)
 
 
 @pytest.mark.gpu

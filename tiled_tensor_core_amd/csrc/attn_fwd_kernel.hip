@@ -54,15 +54,16 @@
 //   * the running maximum m used as the exponent reference moves (and O, l
 //     are rescaled by alpha = exp2((m_old - m_new)*c)) only when some row's
 //     tile maximum exceeds it by more than a margin (in log2 units); else
-//     alpha = 1, and the tile skips the 64 multiplies of O.  fp16 keeps a
-//     stale reference until a row outgrows it by 2^8 (p <= 256).  bf16 uses
-//     2^2 (p <= 4), and corrects for the rounding of P: on a peaky row one
-//     key carries nearly all the weight, and the bf16 rounding of its P (up
-//     to 2^-9 relative) would reach O in full, since l sums the unrounded p.
-//     So for each tile the wave adds bf16(p) - p of the row's largest score
-//     to a per-row term corr (rescaled with l), and O is divided by l + corr:
-//     the dominant key's weight is then the same in O's numerator and
-//     denominator.  LSE uses l alone.  O / l and LSE do not depend on the
+//     alpha = 1, and the tile skips the 64 multiplies of O.  bf16 uses 2^2
+//     (p <= 4), fp16 2^8 (p <= 256).  With a stale reference a row's
+//     largest P is no longer exactly 1, and its 16-bit rounding would reach
+//     O in full if O were divided by the sum of the unrounded p.  So every
+//     row keeps two sums: l, of the unrounded fp32 p (for LSE), and lo, of
+//     the 16-bit P the matrix cores multiply V by (v_dot2c against a pair of
+//     ones, two P per instruction).  O = acc / lo is then a weighted mean of
+//     the rows of V whose weights sum to 1, whatever the rounding of P:
+//     dominant keys and keys tied at the maximum weigh the same in O's
+//     numerator and denominator.  O / lo and LSE do not depend on the
 //     reference.
 //
 // LDS layout: K buffer 0, K buffer 1, V buffer 0, V buffer 1; each a [64][D]
@@ -108,8 +109,9 @@ TTC_INLINE __attribute__((address_space(3))) T* lds_at(int a) {
   return (__attribute__((address_space(3))) T*)(size_t)(uint32_t)a;
 }
 
-// Element-type specific pieces: the 32x32x16 MFMA and the fp32 -> 16-bit
-// pair conversion (round to nearest even) used for the probabilities.
+// Element-type specific pieces: the 32x32x16 MFMA, the fp32 -> 16-bit pair
+// conversion (round to nearest even) used for the probabilities, and the sum
+// of a packed pair.
 template <bool BF16>
 struct Ops;
 
@@ -122,6 +124,11 @@ struct Ops<true> {
   TTC_INLINE static uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
   }
+  // acc + both 16-bit values of a packed pair (v_dot2c against ones)
+  TTC_INLINE static float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+  }
 };
 
 template <>
@@ -132,6 +139,9 @@ struct Ops<false> {
   }
   TTC_INLINE static uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+  TTC_INLINE static float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
   }
 };
 
@@ -196,8 +206,10 @@ constexpr int kLead = 3;       // LDS operand reads issued this many MFMAs ahead
 constexpr int kChunks = 16;    // VALU slices per phase of a pipelined tile
 constexpr int kLoadEvery = 2;  // a pipelined tile issues one K/V tile load every this many steps
 
-// Per-wave state and the work of one key tile.
-template <bool BF16, int D>
+// Per-wave state and the work of one key tile.  FIXED: the wave runs in
+// fixed-reference mode (see the kernel), which also keeps fewer registers
+// live (one K read offset instead of one per k-step).
+template <bool BF16, int D, bool FIXED>
 struct Wave {
   using O = Ops<BF16>;
   static constexpr int BC = kBC;
@@ -215,13 +227,16 @@ struct Wave {
   u32x4 qf[DK];      // Q rows (B operand of S^T = K Q^T)
   f32x16 oacc[DT];   // O^T accumulator of the wave's 32 rows
   u32x4 pb[KB][2];   // 16-bit P^T fragments (B operand of O^T += V^T P^T)
-  float m, l;        // running maximum (raw score units) and row sum
-  float corr;        // bf16: sum of bf16(p) - p of each tile's largest score (reference m)
+  float m, l;        // running maximum (raw score units) and row sum of the fp32 p
+  float lo;          // row sum of the 16-bit P that multiply V (O's normaliser)
   float c, thr;      // score multiplier |scale|*log2(e); margin before m moves
   float alpha;       // pending rescale factor of O and l for the current tile
   float mc;          // m * c, the exponent offset of the current tile
   bool moved;        // some row of the wave moved its reference maximum (alpha != 1)
-  int kro[DK];       // byte offset of this lane's K operand in a K tile, per k-step
+  // byte offset of this lane's K operand in a K tile, per k-step kk; fixed
+  // mode keeps only k-step 0 and forms kk's as kro[0] ^ 32 kk (the swizzle
+  // index and the chunk 2 kk of the operand share no bits)
+  int kro[FIXED ? 1 : DK];
   int vro[DT];       // byte offset of this lane's V^T operand in a V tile, per d-block
 
   TTC_INLINE static float at(const f32x16 (&s)[KB], int v) { return s[v >> 4][v & 15]; }
@@ -229,7 +244,16 @@ struct Wave {
   // ---- MFMA steps -------------------------------------------------------------
   // Score step i (kk = i / KB, kb = i % KB): S^T[kb] += K[kb-th 32 keys][kk] Q^T.
   TTC_INLINE u32x4 kop(int i, const lds_u8* kt) const {
-    return *(const __attribute__((address_space(3))) u32x4*)(kt + kro[i / KB] + (i % KB) * 32 * ROW_BYTES);
+    int kr;
+    if constexpr (FIXED) {
+      // an opaque copy per read: the compiler must not keep all DK offsets live
+      int k0 = kro[0];
+      asm volatile("" : "+v"(k0));
+      kr = (i / KB) == 0 ? k0 : (k0 ^ (32 * (i / KB)));
+    } else {
+      kr = kro[i / KB];
+    }
+    return *(const __attribute__((address_space(3))) u32x4*)(kt + kr + (i % KB) * 32 * ROW_BYTES);
   }
   TTC_INLINE void qk(int i, u32x4 a, f32x16 (&s)[KB]) const {
     const int kk = i / KB, kb = i % KB;
@@ -319,10 +343,6 @@ struct Wave {
     alpha = fast_exp2((m - mref) * c);  // 0 while m is -inf, 1 if m stays
     m = mnew;
     mc = mref * c;
-    if (BF16) {  // p of the tile's largest score, bit-identical to prob()'s
-      const float pm = fast_exp2(__builtin_fmaf(mx, c, -mc));
-      corr = __builtin_fmaf(corr, alpha, (float)(__bf16)pm - pm);
-    }
   }
   TTC_INLINE void max_all(f32x16 (&s)[KB]) {
     float mx = s[0][0];
@@ -344,6 +364,15 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < w; ++i) t[i] = t[i] + t[i + w];
     l = __builtin_fmaf(l, alpha, t[0]);
+    // the same for the packed 16-bit P (after pack()): four chains of four
+    float r4[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      r4[c4] = O::sum2(pb[c4 >> 1][c4 & 1][0], 0.0f);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) r4[c4] = O::sum2(pb[c4 >> 1][c4 & 1][i], r4[c4]);
+    }
+    lo = __builtin_fmaf(lo, alpha, (r4[0] + r4[1]) + (r4[2] + r4[3]));
   }
 
   // ---- one tile without pipelining (masked tiles, short sequences) ----------
@@ -358,8 +387,10 @@ struct Wave {
 #pragma unroll
     for (int k = 0; k < 4 * KB * 2; ++k) pack(s, k);
     row_sum(s);
+    if (moved) {   // wave-uniform: alpha is exactly 1 otherwise
 #pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    }
 #pragma unroll
     for (int i = 0; i < NPV; ++i) pv(i, vop(i, vt));
   }
@@ -374,8 +405,9 @@ struct Wave {
   //     12-15: 4 registers of O^T[0] *= alpha each
   //   phase 2 (NPV steps, MFMA: O^T[t] += V^T P^T, t-major), VALU slices:
   //     4(t-1)..4(t-1)+3: 4 registers of O^T[t] *= alpha each (t >= 1);
-  //     0-7: first level of the row-sum tree (2 adds each); 8-11: second
-  //     level; 12: third; 13: rest, l = alpha l + sum; 12-14: maximum tree
+  //     0-7: first level of the row-sum tree (2 adds each) and two pair
+  //     sums of the packed P each; 8-11: second level; 12: third; 13: rest,
+  //     l = alpha l + sum, lo = alpha lo + packed sum; 12-14: maximum tree
   //     of tile j+1; 15: new reference maximum, alpha, mc of tile j+1
   // RESCALE = false is the variant for tiles whose alpha is exactly 1.
   // ld(k), k = 0 .. NLOAD-1, issues this wave's k-th load of the tiles the
@@ -393,7 +425,7 @@ struct Wave {
     u32x4 op[L];
 #pragma unroll
     for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
-    float rs[NS / 2];
+    float rs[NS / 2], ro[4];
     float mp[10], q[4];
 #pragma unroll
     for (int g = 0; g < NSTEP; ++g) {
@@ -438,6 +470,10 @@ struct Wave {
           if (cc < 8) {
             rs[2 * cc] = at(s, 4 * cc) + at(s, 4 * cc + 1);
             rs[2 * cc + 1] = at(s, 4 * cc + 2) + at(s, 4 * cc + 3);
+            // the packed P of slice cc: dwords 2cc, 2cc+1 of chain cc/2
+            const int c4 = cc >> 1, i0 = 2 * (cc & 1);
+            ro[c4] = O::sum2(pb[c4 >> 1][c4 & 1][i0], (cc & 1) ? ro[c4] : 0.0f);
+            ro[c4] = O::sum2(pb[c4 >> 1][c4 & 1][i0 + 1], ro[c4]);
           } else if (cc < 12) {
             const int k = 2 * (cc - 8);
             rs[k] = rs[2 * k] + rs[2 * k + 1];
@@ -445,6 +481,8 @@ struct Wave {
           } else if (cc == 12) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) rs[k] = rs[2 * k] + rs[2 * k + 1];
+            ro[0] = ro[0] + ro[1];
+            ro[2] = ro[2] + ro[3];
             if (MAXN) {
 #pragma unroll
               for (int k = 0; k < 4; ++k) mp[k] = max3(at(sn, 3 * k), at(sn, 3 * k + 1), at(sn, 3 * k + 2));
@@ -452,6 +490,7 @@ struct Wave {
           } else if (cc == 13) {
             rs[0] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
             l = RESCALE ? __builtin_fmaf(l, alpha, rs[0]) : l + rs[0];
+            lo = RESCALE ? __builtin_fmaf(lo, alpha, ro[0] + ro[2]) : lo + (ro[0] + ro[2]);
             if (MAXN) {
 #pragma unroll
               for (int k = 4; k < 8; ++k) mp[k] = max3(at(sn, 3 * k), at(sn, 3 * k + 1), at(sn, 3 * k + 2));
@@ -466,6 +505,68 @@ struct Wave {
             q[3] = max3(mp[9], at(sn, 30), at(sn, 31));
           } else {
             new_max(max3(q[0], q[1], __builtin_elementwise_maximum(q[2], q[3])));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- one pipelined tile with a fixed exponent reference ---------------------
+  // The step of fixed-reference mode: as pipe_tile, but no maximum, no
+  // rescale, and a schedule that spreads the VALU work evenly over the steps
+  // and keeps three running sums instead of a reduction tree:
+  //   phase 1 (scores of tile j+1), slice cc: p = exp2(s*c - mc) of scores
+  //     2cc, 2cc+1; pack of scores 2cc-2, 2cc-1 (cc >= 1)
+  //   phase 2 (O^T += V^T P^T), slice cc: pack of scores 30, 31 (cc = 0; the
+  //     P V step that reads it is the fourth); scores 2cc, 2cc+1 into two
+  //     chains of l; packed dword cc into the chain of lo; at cc = 15 both
+  //     sums join l and lo.  MASKN: the causal mask of tile j+1 in slices
+  //     8-11, as in pipe_tile.
+  template <int NLOAD, class LD, bool MASKN = false>
+  TTC_INLINE void pipe_tile_fixed(f32x16 (&s)[KB], f32x16 (&sn)[KB], const lds_u8* kt, const lds_u8* vt,
+                                  const LD& ld, int mdelta = 0) {
+    constexpr int L = kLead, NSTEP = NQK + NPV;
+    static_assert(kChunks == 16 && NS == 32, "two scores and one packed dword per slice");
+    u32x4 op[L];
+#pragma unroll
+    for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
+    float ra = 0.0f, rb = 0.0f, rp = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NSTEP; ++g) {
+      const bool p1 = g < NQK;
+      const int i = p1 ? g : g - NQK;
+      const u32x4 a = op[g % L];
+      if (g + L < NSTEP) op[g % L] = (g + L < NQK) ? kop(g + L, kt) : vop(g + L - NQK, vt);
+      if (p1)
+        qk(i, a, sn);
+      else
+        pv(i, a);
+      if (g % kLoadEvery == 0 && g / kLoadEvery < NLOAD) ld(g / kLoadEvery);
+      const int n_steps = p1 ? NQK : NPV;
+      const int c_lo = i * kChunks / n_steps, c_hi = (i + 1) * kChunks / n_steps;
+#pragma unroll
+      for (int cc = c_lo; cc < c_hi; ++cc) {
+        if (p1) {
+          prob(s, 2 * cc);
+          prob(s, 2 * cc + 1);
+          if (cc >= 1) pack(s, cc - 1);
+        } else {
+          if (cc == 0) pack(s, 15);
+          if (MASKN && cc >= 8 && cc < 12) {
+            if constexpr (D == 128) {
+              diag_mask8(sn, mdelta, 8 * (cc - 8));
+            } else {
+#pragma unroll
+              for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
+            }
+          }
+          ra = cc == 0 ? at(s, 0) : ra + at(s, 2 * cc);
+          rb = cc == 0 ? at(s, 1) : rb + at(s, 2 * cc + 1);
+          rp = O::sum2(pb[cc >> 3][(cc >> 2) & 1][cc & 3], rp);
+          if (cc == 15) {
+            l += ra + rb;
+            lo += rp;
           }
         }
       }
@@ -496,11 +597,6 @@ TTC_INLINE void load_one(u32x4 rs, lds_u8* dst, int off, int soff) {
                : "memory", "m0");
 }
 
-template <int PER_W, int ROW_BYTES, int BC>
-TTC_INLINE void load_tile(u32x4 rs, lds_u8* dst, const int* off, int j) {
-#pragma unroll
-  for (int t = 0; t < PER_W; ++t) load_one(rs, dst + t * 1024, off[t], j * BC * ROW_BYTES);
-}
 
 // The same descriptor as head_rsrc below, as four dwords: base address
 // (48 bits, stride 0), size in bytes, and the format word.
@@ -518,14 +614,15 @@ TTC_INLINE __amdgpu_buffer_rsrc_t head_rsrc(const void* base, unsigned nbytes) {
 // Stores of O are marked non-temporal (cache policy bit 1, "nt" on gfx950):
 // O is written once, and keeping it out of L2 leaves room for the K/V tiles
 // the other query blocks of a head still read.
-TTC_INLINE void store_b128(__amdgpu_buffer_rsrc_t rs, f32x4 v, int voff) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 2);
+TTC_INLINE void store_b128(__amdgpu_buffer_rsrc_t rs, f32x4 v, unsigned voff) {
+  // the hardware reads the 32-bit offset as unsigned
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)voff, 0, 2);
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool FIXED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
-  using W = Wave<BF16, D>;
+  using W = Wave<BF16, D, FIXED>;
   using S = Swz<D>;
   constexpr int BC = kBC, NW = kNW, BM = kBM;
   constexpr int KB = W::KB, DK = W::DK, DT = W::DT;
@@ -606,18 +703,28 @@ attn_fwd_kernel(AttnParams p) {
   // the start of every item (from a lane number the compiler cannot see
   // through) rather than kept live across items, where they would only take
   // up registers in the epilogue.
+  // A wave's load t of a tile covers the rows 64t/CPR after those of its
+  // load 0.  The V swizzle depends only on row bits those rows share, so V
+  // load t fetches at the lane offset of load 0 plus 1 KiB * t; the K swizzle
+  // adds 4t to the swizzle index (both head dims), so K load t fetches at
+  // (lane offset of load 0) ^ 64t, plus 1 KiB * t.  The 1 KiB * t goes into
+  // the scalar offset: one VGPR each for all K and all V loads.
   const int first_idx = wave * PER_W * 64 + lane;   // LDS chunk index of this lane's first load
-  auto lane_offsets = [&](int ln, int (&ko)[PER_W], int (&vo)[PER_W]) {
-#pragma unroll
-    for (int t = 0; t < PER_W; ++t) {
-      const int idx = wave * PER_W * 64 + ln + 64 * t;
-      const int r = idx / CPR, slot = idx % CPR;
-      ko[t] = r * ROW_BYTES + ((slot ^ S::k(r)) << 4);
-      vo[t] = r * ROW_BYTES + ((slot ^ S::v(r)) << 4);
-    }
+  auto lane_offsets = [&](int ln, int& ko, int& vo) {
+    const int idx = wave * PER_W * 64 + ln;
+    const int r = idx / CPR, slot = idx % CPR;
+    ko = r * ROW_BYTES + ((slot ^ S::k(r)) << 4);
+    vo = r * ROW_BYTES + ((slot ^ S::v(r)) << 4);
   };
-  int koff[PER_W], voff[PER_W];
+  int koff, voff;
   lane_offsets(lane, koff, voff);
+  // lane offset of K load t (an opaque copy, so the compiler does not keep
+  // all PER_W of them live across the loop)
+  auto koff_t = [&](int t) {
+    int k = koff;
+    asm volatile("" : "+v"(k));
+    return t == 0 ? k : (k ^ (64 * t));
+  };
   // The last tile's rows past N (if any) repeat row N-1 (finite values whose
   // scores are masked, so they add exactly 0), keeping the swizzled slot of
   // the row they stand in for.
@@ -630,15 +737,17 @@ attn_fwd_kernel(AttnParams p) {
     return (min(r, N - 1 - j_tail * BC) - r) * ROW_BYTES;
   };
   const int wofs = wave * PER_W * 1024;   // this wave's share of a tile
-  auto load_kv = [&](u32x4 rs, const int (&off)[PER_W], lds_u8* buf, int j) {
-    if (j == j_tail) {
-      int o[PER_W];
+  // K tile j
+  auto load_k = [&](u32x4 rs, lds_u8* buf, int j) {
 #pragma unroll
-      for (int t = 0; t < PER_W; ++t) o[t] = off[t] + tail_delta(t);
-      load_tile<PER_W, ROW_BYTES, BC>(rs, buf + wofs, o, j);
-    } else {
-      load_tile<PER_W, ROW_BYTES, BC>(rs, buf + wofs, off, j);
-    }
+    for (int t = 0; t < PER_W; ++t)
+      load_one(rs, buf + wofs + t * 1024, koff_t(t) + (j == j_tail ? tail_delta(t) : 0), j * TILE_BYTES + t * 1024);
+  };
+  // V tile j: load t at lane offset vo + 1 KiB * t (scalar part)
+  auto load_v = [&](u32x4 rs, int vo, lds_u8* buf, int j) {
+#pragma unroll
+    for (int t = 0; t < PER_W; ++t)
+      load_one(rs, buf + wofs + t * 1024, vo + (j == j_tail ? tail_delta(t) : 0), j * TILE_BYTES + t * 1024);
   };
 
   // ---- per-lane LDS read offsets within a tile ------------------------------------
@@ -646,7 +755,7 @@ attn_fwd_kernel(AttnParams p) {
     const int krow = ln & 31;                     // key row within a 32-key block
     const int kchunk = ln >> 5;                   // + 2*kk
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
+    for (int kk = 0; kk < (FIXED ? 1 : DK); ++kk)
       w.kro[kk] = krow * ROW_BYTES + (((2 * kk + kchunk) ^ S::k(krow)) << 4);
     const int g = ln >> 4, gj = ln & 15;          // 16-lane group for the V reads
     const int vkey = 4 * (g >> 1) + (gj >> 2);    // + 32*kb + 16*h (and + 8)
@@ -702,18 +811,29 @@ attn_fwd_kernel(AttnParams p) {
   u32x4 vrs = load_rsrc(p.v + (size_t)bh * N * D, HEAD_BYTES);
   int n_tiles = tiles_of(qb);
   load_q(bh, qb);
-  load_kv(krs, koff, K0, 0);
-  load_kv(vrs, voff, V0, 0);
-  if (1 < n_tiles) load_kv(krs, koff, K1, 1);
+  load_k(krs, K0, 0);
+  load_v(vrs, voff, V0, 0);
+  if (1 < n_tiles) load_k(krs, K1, 1);
   bool v0_late = false;
   f32x16 sa[KB], sb[KB];
+  // Fixed-reference mode (FIXED): an item keeps the maximum of its first
+  // tile (raised by p.headroom log2 units) as each row's exponent reference
+  // throughout, so no later tile needs its maximum or a rescale of O.  O / lo is exact whatever the
+  // reference; only the range of P depends on it.  Every P, and every P V
+  // sum, stays finite while the row sums lo do (fp16: lo finite; bf16: lo at
+  // most p.l_max = 2^48, which also leaves P V sums far from overflow).  A
+  // wave whose lo does not (or is NaN) leaves item index + 1 in redo_tag,
+  // and the workgroup computes that item again with each row's exact
+  // maximum as its reference (found by a pass over the item's K tiles
+  // first), so every p <= 1; the item's O and LSE are overwritten.  The tag
+  // is read after the barrier that starts the next item (after the last
+  // item, after one more barrier), and written only in an epilogue, at
+  // least one barrier later.
+  __shared__ int redo_tag;
+  if (FIXED && threadIdx.x == 0) redo_tag = -1;
+  int redone = -1;     // the tag of the last item computed again
 
   for (;;) {
-    const int q0 = qb * BM;
-    const size_t head_off = (size_t)bh * (size_t)N * D;
-    const int wr0 = q0 + wave * 32;              // first query row of this wave
-    const int qrow = wr0 + (lane & 31);          // this lane's query row
-
     {
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -723,21 +843,37 @@ attn_fwd_kernel(AttnParams p) {
     // the item's loads have landed, and every wave is done with the previous
     // item's buffers
     wait_all();
-    if (v0_late) load_kv(vrs, voff, V0, 0);
+    bool exact = false;   // this item is computed again, with exact row maxima
+    if constexpr (FIXED) {
+      const int tag = __builtin_amdgcn_readfirstlane(redo_tag);
+      if (tag == t_item && tag != redone) {
+        // the previous item's P left the fixed reference's range: load its
+        // operands again (over the next item's, which are loaded again later)
+        redone = tag;
+        --t_item;
+        item(t_item, bh, qb);
+        krs = load_rsrc(p.k + (size_t)bh * N * D, HEAD_BYTES);
+        vrs = load_rsrc(p.v + (size_t)bh * N * D, HEAD_BYTES);
+        n_tiles = tiles_of(qb);
+        load_q(bh, qb);
+        load_k(krs, K0, 0);
+        load_v(vrs, voff, V0, 0);
+        if (1 < n_tiles) load_k(krs, K1, 1);
+        v0_late = false;
+        wait_all();
+        exact = true;
+      }
+    }
+    if (v0_late) load_v(vrs, voff, V0, 0);
     if (p.q_mode != 0) {
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk)   // negative scale: flip every sign; zero scale: zero
         w.qf[kk] = p.q_mode == 1 ? (w.qf[kk] ^ 0x80008000u) : (u32x4){0, 0, 0, 0};
     }
-
-    // ---- running state -------------------------------------------------------
-    w.m = -INFINITY;
-    w.l = 0.0f;
-    w.corr = 0.0f;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) w.oacc[t][r] = 0.0f;
+    const int q0 = qb * BM;
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const int wr0 = q0 + wave * 32;              // first query row of this wave
+    const int qrow = wr0 + (lane & 31);          // this lane's query row
 
     // mask limit of tile j for this lane (see Wave::mask), and whether any row
     // of this wave needs the mask there
@@ -750,10 +886,43 @@ attn_fwd_kernel(AttnParams p) {
       else
         W::mask(s, mask_lim(j));
     };
+
+    // ---- exact row maxima of an item computed again (rare) -------------------
+    // The item's K tiles stream through the two K buffers (tile j in buffer
+    // j % 2, K_0 and K_1 already loaded) for the scores and their maximum;
+    // then K_0 and K_1 are loaded again for the item itself.
+    float m_exact = -INFINITY;
+    if constexpr (FIXED) {
+      if (exact) {
+        for (int jj = 0; jj < n_tiles; ++jj) {
+          if (jj > 0) wait_all();   // K_jj landed; every wave is done with tile jj-1
+          if (jj > 0 && jj + 1 < n_tiles) load_k(krs, ((jj + 1) & 1) ? K1 : K0, jj + 1);
+          w.scores(sa, (jj & 1) ? K1 : K0);
+          apply_mask(sa, jj);
+#pragma unroll
+          for (int v = 0; v < W::NS; ++v) m_exact = __builtin_elementwise_maximum(m_exact, W::at(sa, v));
+        }
+        m_exact = pair_max(m_exact);
+        wait_all();
+        load_k(krs, K0, 0);
+        if (1 < n_tiles) load_k(krs, K1, 1);
+        wait_all();
+      }
+    }
+
+    // ---- running state -------------------------------------------------------
+    w.m = -INFINITY;
+    w.l = 0.0f;
+    w.lo = 0.0f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.oacc[t][r] = 0.0f;
+
     // Tiles no row of the workgroup needs masked run software-pipelined: step j
-    // handles tile j and computes tile j+1's scores and maximum, so both must
-    // be such tiles; its loads (K_{j+2}, V_{j+1}) must not reach the tile that
-    // ends past N.  The rest run in a plain loop.
+    // handles tile j and computes tile j+1's scores (and, in running-maximum
+    // mode, maximum), so both must be such tiles; its loads (K_{j+2}, V_{j+1})
+    // must not reach the tile that ends past N.  The rest run in a second loop.
     const int n_full = CAUSAL ? min(q0 / BC, N / BC) : N / BC;
     int n_pipe = max(0, min(n_full, n_tiles) - 1);
     if (n_tiles > N / BC) n_pipe = max(0, min(n_pipe, N / BC - 2));
@@ -763,7 +932,23 @@ attn_fwd_kernel(AttnParams p) {
     // one tile ahead): wait for K_{j+1}, V_j; start K_{j+2}, V_{j+1}; compute.
     w.scores(sa, K0);
     apply_mask(sa, 0);
-    w.max_all(sa);
+    if constexpr (FIXED) {
+      // the reference is the first tile's maximum (or the exact one) for the
+      // whole item; O, l, lo start at 0, so alpha never applies
+      if (exact) {
+        w.m = m_exact;
+        w.mc = (m_exact == -INFINITY ? 0.0f : m_exact) * w.c;
+      } else {
+        // p_max * 2^-headroom for the first tile: later tiles may outgrow it
+        // by 2^headroom before P nears the range bound
+        w.max_all(sa);
+        w.mc += p.headroom;
+      }
+      w.moved = false;
+      w.alpha = 1.0f;
+    } else {
+      w.max_all(sa);
+    }
 
     // Pipelined step j loads K_{j+2} (if any) into the K buffer tile j used and
     // V_{j+1} into the other V buffer, both wholly inside the sequence, one
@@ -771,30 +956,34 @@ attn_fwd_kernel(AttnParams p) {
     int j = 0;
     auto ld_even = [&](int k) {
       if (k < PER_W) {
-        if (j + 2 < n_tiles) load_one(krs, K0 + wofs + k * 1024, koff[k], (j + 2) * TILE_BYTES);
+        if (j + 2 < n_tiles) load_one(krs, K0 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
       } else {
-        load_one(vrs, V1 + wofs + (k - PER_W) * 1024, voff[k - PER_W], (j + 1) * TILE_BYTES);
+        load_one(vrs, V1 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
     };
     auto ld_odd = [&](int k) {
       if (k < PER_W) {
-        if (j + 2 < n_tiles) load_one(krs, K1 + wofs + k * 1024, koff[k], (j + 2) * TILE_BYTES);
+        if (j + 2 < n_tiles) load_one(krs, K1 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
       } else {
-        load_one(vrs, V0 + wofs + (k - PER_W) * 1024, voff[k - PER_W], (j + 1) * TILE_BYTES);
+        load_one(vrs, V0 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
     };
     constexpr int NL = 2 * PER_W;
     for (; j + 1 < n_pipe; j += 2) {
       wait_all();
       progress();
-      if (w.moved)
+      if constexpr (FIXED)   // no maximum, no rescale
+        w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
+      else if (w.moved)
         w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
       else
         w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
       ++j;
       wait_all();
       progress();
-      if (w.moved)
+      if constexpr (FIXED)
+        w.template pipe_tile_fixed<NL>(sb, sa, K0, V1, ld_odd);
+      else if (w.moved)
         w.template pipe_tile<true, NL>(sb, sa, K0, V1, ld_odd);
       else
         w.template pipe_tile<false, NL>(sb, sa, K0, V1, ld_odd);
@@ -803,7 +992,9 @@ attn_fwd_kernel(AttnParams p) {
     if (j < n_pipe) {
       wait_all();
       progress();
-      if (w.moved)
+      if constexpr (FIXED)
+        w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
+      else if (w.moved)
         w.template pipe_tile<true, NL>(sa, sb, K1, V0, ld_even);
       else
         w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
@@ -820,12 +1011,12 @@ attn_fwd_kernel(AttnParams p) {
       const bool odd = j & 1;
       if (k < PER_W) {
         if (j + 2 < n_tiles)
-          load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, koff[k] + (j + 2 == j_tail ? tail_delta(k) : 0),
-                   (j + 2) * TILE_BYTES);
+          load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, koff_t(k) + (j + 2 == j_tail ? tail_delta(k) : 0),
+                   (j + 2) * TILE_BYTES + k * 1024);
       } else {
         const int t = k - PER_W;
-        load_one(vrs, (odd ? V0 : V1) + wofs + t * 1024, voff[t] + (j + 1 == j_tail ? tail_delta(t) : 0),
-                 (j + 1) * TILE_BYTES);
+        load_one(vrs, (odd ? V0 : V1) + wofs + t * 1024, voff + (j + 1 == j_tail ? tail_delta(t) : 0),
+                 (j + 1) * TILE_BYTES + t * 1024);
       }
     };
     for (; j + 1 < n_tiles; ++j) {
@@ -837,19 +1028,24 @@ attn_fwd_kernel(AttnParams p) {
       if constexpr (CAUSAL) {
         // a causal diagonal tile, masked in the pipeline (keys past N follow
         // every row below N, so the causal mask hides them as well)
-        if (w.moved)
+        if constexpr (FIXED)
+          w.template pipe_tile_fixed<NL, decltype(ld_any), true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
+                                                                 (j + 1) * BC - wr0);
+        else if (w.moved)
           w.template pipe_tile<true, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
                                                                        (j + 1) * BC - wr0);
         else
           w.template pipe_tile<false, NL, decltype(ld_any), true, true>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any,
                                                                         (j + 1) * BC - wr0);
       } else {
-        if (w.moved)
+        if constexpr (FIXED)
+          w.template pipe_tile_fixed<NL>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
+        else if (w.moved)
           w.template pipe_tile<true, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
         else
           w.template pipe_tile<false, NL, decltype(ld_any), false>(sa, sb, odd ? K0 : K1, odd ? V1 : V0, ld_any);
         apply_mask(sb, j + 1);
-        w.max_all(sb);
+        if constexpr (!FIXED) w.max_all(sb);
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
@@ -867,11 +1063,11 @@ attn_fwd_kernel(AttnParams p) {
     const int n_tiles2 = tiles_of(qb2);
     const bool last_odd = j & 1;
     if (more) {
-      load_kv(krs2, koff, K0, 0);
-      if (1 < n_tiles2) load_kv(krs2, koff, K1, 1);
-      if (last_odd) load_kv(vrs2, voff, V0, 0);
+      load_k(krs2, K0, 0);
+      if (1 < n_tiles2) load_k(krs2, K1, 1);
+      if (last_odd) load_v(vrs2, voff, V0, 0);
     }
-    // ---- epilogue: O = acc / (l + corr), LSE = ln2 * (m*c + log2 l) ----------
+    // ---- epilogue: O = acc / lo, LSE = ln2 * (mc + log2 l) --------------------
     // A lane holds 4-float pieces of one row of O, so storing from the
     // accumulators writes 32 bytes into each of 32 rows per instruction.
     // Instead each wave turns every 32x32 block of O row-major in a private
@@ -880,7 +1076,7 @@ attn_fwd_kernel(AttnParams p) {
     // whole 128-byte row pieces.
     auto epilogue = [&](lds_u8* stage) {
       const float lt = pair_sum(w.l);
-      const float inv = __builtin_amdgcn_rcpf(BF16 ? lt + w.corr : lt);
+      const float inv = __builtin_amdgcn_rcpf(pair_sum(w.lo));
       // lane-derived offsets computed here, not hoisted out of the item loop
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -890,7 +1086,9 @@ attn_fwd_kernel(AttnParams p) {
       // O of the head as a buffer: the rows past N-1 of a ragged last block
       // fall outside it and their stores are dropped
       const __amdgpu_buffer_rsrc_t ors = head_rsrc(p.o + head_off, (unsigned)N * D * 4);
-      const int vo = (wr0 + rs) * (D * 4) + cs * 16;
+      // unsigned byte offsets: the host admits heads whose fp32 O (plus the
+      // rows of a ragged last block) spans up to 2^32 - 1 bytes
+      const unsigned vo = (unsigned)(wr0 + rs) * (unsigned)(D * 4) + (unsigned)(cs * 16);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
 #pragma unroll
@@ -903,11 +1101,11 @@ attn_fwd_kernel(AttnParams p) {
         for (int s8 = 0; s8 < 4; ++s8) {
           const int row = 8 * s8 + rs;
           const f32x4 val = *(const lds_f32x4*)(stage + row * 128 + ((cs ^ ((row >> 1) & 7)) << 4));
-          store_b128(ors, val, vo + s8 * 8 * D * 4 + t * 128);
+          store_b128(ors, val, vo + (unsigned)(s8 * 8 * D * 4 + t * 128));
         }
       }
       if (qrow < N && lane < 32)
-        p.lse[(size_t)bh * N + qrow] = (w.m * w.c + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+        p.lse[(size_t)bh * N + qrow] = (w.mc + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
     };
     // a wave whose rows all precede the tile's first key has nothing to do
     if (!CAUSAL || j * BC <= wr0 + 31) w.finish(sa, last_odd ? V1 : V0);
@@ -926,7 +1124,19 @@ attn_fwd_kernel(AttnParams p) {
       }
       epilogue(V1 + wave * 4096);
     }
-    if (!more) break;
+    if constexpr (FIXED) {
+      // vote: some P (or a sum of P V) may have left its range
+      if (!exact && __builtin_amdgcn_ballot_w64(!(w.lo <= p.l_max)) != 0 && lane == 0) redo_tag = t_item + 1;
+    }
+    if (!more) {
+      if constexpr (!FIXED) break;
+      if (exact) break;
+      __syncthreads();   // every wave's tag is written
+      if (__builtin_amdgcn_readfirstlane(redo_tag) != t_item + 1) break;
+      ++t_item;          // the loop head computes item t_item - 1 again
+      v0_late = false;
+      continue;
+    }
     ++t_item;
     bh = bh2;
     qb = qb2;
@@ -939,9 +1149,9 @@ attn_fwd_kernel(AttnParams p) {
 
 // ---- launch ------------------------------------------------------------------
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool FIXED>
 static const void* kernel_fn() {
-  return reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL>);
+  return reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, FIXED>);
 }
 
 int block_rows(int d) {
@@ -953,7 +1163,7 @@ int block_rows(int d) {
 // (compute units x workgroups per compute unit), cached per device.
 static int resident_groups(int variant, const void* fn) {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[8][kMaxDev];
+  static std::atomic<int> cache[16][kMaxDev];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (dev >= 0 && dev < kMaxDev) {
@@ -968,18 +1178,25 @@ static int resident_groups(int variant, const void* fn) {
   return n;
 }
 
-static const void* variant_fn(bool bf16, int d, bool causal) {
-  return bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true>() : kernel_fn<true, 64, false>())
-                         : (causal ? kernel_fn<true, 128, true>() : kernel_fn<true, 128, false>()))
-              : (d == 64 ? (causal ? kernel_fn<false, 64, true>() : kernel_fn<false, 64, false>())
-                         : (causal ? kernel_fn<false, 128, true>() : kernel_fn<false, 128, false>()));
+template <bool FIXED>
+static const void* variant_fn_m(bool bf16, int d, bool causal) {
+  return bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true, FIXED>() : kernel_fn<true, 64, false, FIXED>())
+                         : (causal ? kernel_fn<true, 128, true, FIXED>() : kernel_fn<true, 128, false, FIXED>()))
+              : (d == 64 ? (causal ? kernel_fn<false, 64, true, FIXED>() : kernel_fn<false, 64, false, FIXED>())
+                         : (causal ? kernel_fn<false, 128, true, FIXED>() : kernel_fn<false, 128, false, FIXED>()));
+}
+
+static const void* variant_fn(bool bf16, int d, bool causal, bool fixed) {
+  return fixed ? variant_fn_m<true>(bf16, d, causal) : variant_fn_m<false>(bf16, d, causal);
 }
 
 hipError_t resolve_cfg(bool bf16, int d, bool causal, const AttnParams& prm, LaunchCfg& cfg) {
   const long long n_qblk = (prm.N + block_rows(d) - 1) / block_rows(d);
   const long long items = (long long)prm.BH * n_qblk;
-  const int variant = (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
-  const int slots = resident_groups(variant, variant_fn(bf16, d, causal));
+  if (cfg.mode == 0) cfg.mode = 1;
+  const bool fixed = cfg.mode == 1;
+  const int variant = (fixed ? 8 : 0) + (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
+  const int slots = resident_groups(variant, variant_fn(bf16, d, causal, fixed));
   if (slots < 0) return hipErrorInvalidDevice;
   // built-in: heads split over the 8 XCDs when they divide evenly, as many
   // workgroups as run at once, groups of heads that fill one round of items.
@@ -1009,9 +1226,22 @@ hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const 
   const int bm = block_rows(d);
   prm.n_qblk = (prm.N + bm - 1) / bm;
   // raw-score margin before the reference maximum moves: 2^2 in probability
-  // units for bf16 (whose kernel corrects the rounding of each tile's largest
-  // P), 2^8 for fp16
+  // units for bf16, 2^8 for fp16 (O is divided by the sum of the rounded P,
+  // so the margin changes no weight of O, only the range of P)
   prm.thr = fminf((bf16 ? 2.0f : 8.0f) / prm.c, 3.0e38f);
+  // fixed-reference mode (cfg.mode 1) unless the caller asked for the
+  // running maximum.  Bound on a lane's sum lo of the 16-bit P (so on each
+  // of them) before the item is computed again: bf16 P keep fp32's exponent
+  // range, and 2^48 leaves the P V sums far from overflow; fp16 P are finite
+  // exactly when their sum is.
+  const bool fixed = cfg.mode != 2;
+  prm.l_max = bf16 ? 281474976710656.0f : 3.402823466e38f;
+  // The fixed reference sits this many log2 units above the first tile's
+  // maximum, so a row may outgrow its first tile by 2^(48 + 48) (bf16) or
+  // 2^(16 + 4) (fp16) before its item is computed again.  The first tile's
+  // largest p is then 2^-48: fp32 and bf16 keep 126 binades below 1, so the
+  // terms that matter stay normal.  fp16 has 14, hence its smaller headroom.
+  prm.headroom = bf16 ? 48.0f : 4.0f;
   const long long items = (long long)prm.BH * prm.n_qblk;
   if (items > (1LL << 30)) return hipErrorInvalidConfiguration;
   prm.n_dom = cfg.n_dom;
@@ -1020,7 +1250,7 @@ hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const 
   prm.prio = cfg.prio == 1 ? 1 : 0;
   const int grid = prm.n_dom * prm.n_work;
   void* args[] = {&prm};
-  return hipLaunchKernel(variant_fn(bf16, d, causal), dim3(grid), dim3(kNW * 64), args, 0, stream);
+  return hipLaunchKernel(variant_fn(bf16, d, causal, fixed), dim3(grid), dim3(kNW * 64), args, 0, stream);
 }
 
 }  // namespace ttc

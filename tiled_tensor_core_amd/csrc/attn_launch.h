@@ -21,6 +21,10 @@ struct AttnParams {
   float thr;           // raw-score margin before the running maximum moves (set by the launcher)
   int q_mode;          // 0: use Q; 1: use -Q (negative scale); 2: use 0 (zero scale)
   int prio;            // 1: workgroups set their wave priority by progress; 0: they do not
+  float l_max;         // fixed-reference mode: bound on a lane's sum of the 16-bit P before
+                       // its item is computed again (set by the launcher)
+  float headroom;      // fixed-reference mode: log2 units between the first tile's maximum
+                       // and the reference (set by the launcher)
 };
 
 // Launch configuration; a field of 0 takes the built-in choice.
@@ -29,6 +33,7 @@ struct LaunchCfg {
   int n_work;   // persistent workgroups per domain
   int grp;      // heads per group in a domain's item order
   int prio;     // 1 on, 2 off
+  int mode;     // exponent reference: 1 fixed per item, 2 running maximum
 };
 
 // Query rows per workgroup for head dim d.
