@@ -22,6 +22,10 @@ about 10 %.
 MLP up-projection workload (M=16384 tokens, K=4096, N=16384): 2*M*N*K FLOPs
 against the dense bf16 MFMA peak.
 
+``--kernel unfused`` times ``attn_fwd_unfused`` (scores in HBM, row softmax, P V)
+on the same workload and reports its TFLOP/s (same FLOP count) and the HBM
+roofline of its three-kernel step.
+
 ``--kernel softmax`` times the row-wise softmax entry point ``softmax_rows``
 instead: a step is one softmax over a [rows, cols] matrix resident in HBM,
 reported in GB/s of algorithmic traffic (each element read once and written
@@ -53,6 +57,9 @@ SOFTMAX_METRIC = "row softmax GB/s (algorithmic bytes: one read and one write pe
 SOFTMAX_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "softmax_kernel.hip")
 GEMM_METRIC = "GEMM + bias + GELU TFLOP/s (2*M*N*K) + % of MI355X bf16 MFMA peak"
 GEMM_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "gemm_kernel.hip")
+UNFUSED_METRIC = ("un-fused attention fwd (scores in HBM, row softmax, P V) TFLOP/s + HBM roofline of the "
+                  "three-kernel step")
+UNFUSED_SRC = os.path.join(ROOT, "tiled_tensor_core_amd", "csrc", "unfused_kernel.hip")
 
 
 def flops(B, H, N, d, causal):
@@ -394,13 +401,86 @@ def run_gemm(a, torch, attn, synth):
     print(json.dumps(out), flush=True)
 
 
+def unfused_bytes(B, H, N, d, causal):
+    """Algorithmic HBM bytes of the un-fused path: the score matrix written
+    (fp32), read and written by the row softmax, and read by P V (causal:
+    only the N(N+1)/2 visible entries need reading); Q, K, V read once; O
+    (fp32) and LSE written once."""
+    bh = B * H
+    vis = N * (N + 1) // 2 if causal else N * N
+    return 4.0 * bh * (3 * N * N + vis) + bh * N * d * (3 * 2 + 4) + bh * N * 4
+
+
+def run_unfused(a, torch, attn, synth):
+    w = synth.WORKLOADS[a.workload]
+    causal = w.causal[-1]
+    print(f"[bench] generating {w.name} inputs {w.describe()}", file=sys.stderr, flush=True)
+    bits = synth.make_workload(w)
+    q, k, v = (synth.to_torch(x, w.dtype, "cuda") for x in bits)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    need = attn.attn_unfused_workspace_bytes(B, H, N)
+    ws = torch.empty((need // 4,), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} un-fused steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
+    launch = lambda: attn.attn_fwd_unfused(q, k, v, o, lse, ws, need, B, H, N, d, causal, w.scale, stream)
+    r = time_launches(torch, launch, stream, a.steps, a.warmup, a.warmup_seconds)
+    f = flops(B, H, N, d, causal)
+    nbytes = unfused_bytes(B, H, N, d, causal)
+    value = f / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = nbytes / (r["kernel_ms_mean"] * 1e-3) / 1e9
+    traffic = measured_traffic(os.path.join(ROOT, "profiles", f"unfused_{w.name}_traffic.txt"), UNFUSED_SRC)
+    out = {
+        "metric": UNFUSED_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"un-fused attention fwd {'causal' if causal else 'non-causal'} {w.describe()}",
+            "B": B, "H": H, "N": N, "d": d, "causal": causal, "workspace_bytes": need,
+            "parallelism": "none (1 GPU)",
+        },
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": nbytes,
+            "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+            "kernel_ms_median": round(r["kernel_ms_median"], 5),
+            "kernel_ms_min": round(r["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(r["kernel_ms_p90"], 5),
+            "note": "the three launches of one step (scores, row softmax, P V) between one event pair",
+        },
+    }
+    if not a.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{a.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, causal, bits, a.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama")
-    ap.add_argument("--kernel", choices=["attention", "softmax", "gemm"], default="attention",
+    ap.add_argument("--kernel", choices=["attention", "softmax", "gemm", "unfused"], default="attention",
                     help="which entry point to time (default: the attention forward pass)")
     ap.add_argument("--softmax-workload", default="scores")
     ap.add_argument("--gemm-workload", default="mlp")
@@ -408,6 +488,8 @@ def main():
                     help="run attention with the launch configuration cached by tiled_tensor_core_amd.tune "
                          "for this workload (attn_fwd_cfg) instead of the built-in one (attn_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-noncausal", action="store_true",
+                    help="skip timing the causal workload's inputs without the mask")
     ap.add_argument("--warmup-seconds", type=float, default=WARMUP_MIN_S,
                     help="minimum warm-up time in seconds (0: exactly --warmup steps, as counter runs want)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -448,6 +530,9 @@ def main():
         return
     if a.kernel == "gemm":
         run_gemm(a, torch, attn, synth)
+        return
+    if a.kernel == "unfused":
+        run_unfused(a, torch, attn, synth)
         return
     w = synth.WORKLOADS[a.workload]
     causal = w.causal[-1]
@@ -502,6 +587,19 @@ def main():
             "kernel_ms_p90": round(r["kernel_ms_p90"], 5),
         },
     }
+    if causal and not a.no_noncausal:
+        # the same inputs without the causal mask, timed the same way (the
+        # metric names both masks)
+        rn = time_workload(attn, torch, w, False, a.steps, a.warmup, inputs, a.warmup_seconds, None)
+        out["noncausal"] = {
+            "value": round(rn["flops"] / (rn["ms_per_step"] * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(rn["ms_per_step"], 5),
+            "kernel_ms_mean": round(rn["kernel_ms_mean"], 5),
+            "frac": round(rn["flops"] / (rn["kernel_ms_mean"] * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+            "workload": f"attention fwd non-causal {w.describe()}",
+        }
+        print("[bench] timed the non-causal mask", file=sys.stderr, flush=True)
     if a.extra:
         per = {}
         for name, ow in synth.WORKLOADS.items():

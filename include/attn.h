@@ -65,7 +65,8 @@ enum attn_status {
   ATTN_ERR_SCALE = 7,          /* scale is NaN or infinite                       */
   ATTN_ERR_CAUSAL = 8,         /* causal is not 0 or 1                           */
   ATTN_ERR_ALIAS = 9,          /* o or lse overlaps another buffer               */
-  ATTN_ERR_CONFIG = 10         /* a launch configuration field is out of range   */
+  ATTN_ERR_CONFIG = 10,        /* a launch configuration field is out of range   */
+  ATTN_ERR_WORKSPACE = 11      /* workspace NULL, too small or misaligned        */
 };
 
 enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
@@ -155,6 +156,34 @@ int attn_fwd_cfg(const void* q, const void* k, const void* v, float* o, float* l
  * call, cached per device); enqueues nothing.  Returns an attn_status code
  * (ATTN_ERR_HIP if the device query fails). */
 int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_launch_cfg* cfg);
+
+/* Un-fused attention forward: the same operation, outputs and argument
+ * rules as attn_fwd, computed the way the FlashAttention section of the
+ * TileLang tutorial says the fused kernel avoids -- with the N x N score
+ * matrix in device memory.  Three kernels run on `stream`:
+ *   1. S = scale * Q K^T in fp32 (causal: -inf above the diagonal) into the
+ *      workspace, as a [B*H, N, N] row-major array;
+ *   2. the row softmax of softmax.h, in place on S, which also writes lse;
+ *   3. O = P V, P rounded to q's type (as the fused kernel rounds its
+ *      probabilities), fp32 accumulation.
+ * It exists to measure what fusion saves (its S traffic is 16 B*H*N^2
+ * bytes), and as a second, independent HIP path for the same result.
+ *
+ *   workspace        device pointer, 16-byte aligned, at least
+ *                    attn_unfused_workspace_bytes(B, H, N) bytes; owned by
+ *                    the caller, overwritten, must not overlap q, k, v, o,
+ *                    lse; the stream must finish with it before it is reused.
+ *   workspace_bytes  its size in bytes.
+ * Limits beyond attn_fwd's: B*H <= 65535 and B*H*N < 2^31.  Errors: as
+ * attn_fwd, plus ATTN_ERR_WORKSPACE (NULL, misaligned or too small; no
+ * device work is enqueued). */
+int attn_fwd_unfused(const void* q, const void* k, const void* v, float* o, float* lse,
+                     void* workspace, unsigned long long workspace_bytes, int B, int H, int N,
+                     int d, int causal, float scale, void* stream, int dtype);
+
+/* Bytes of workspace attn_fwd_unfused needs: B*H*N*N*4 (0 if the shape is
+ * outside its limits). */
+unsigned long long attn_unfused_workspace_bytes(int B, int H, int N);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* attn_status_str(int status);

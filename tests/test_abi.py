@@ -299,3 +299,41 @@ def test_binding_checks_softmax_and_gemm_tensors():
         attn.gemm_bf16(a, w, b[:8], torch.zeros((16, 24), dtype=torch.bfloat16), 16, 24, 32, stream=0)
     with pytest.raises(ValueError, match="on a GPU"):
         attn.gemm_bf16(a, w, b, torch.zeros((16, 24), dtype=torch.bfloat16), 16, 24, 32, stream=0)
+
+
+# ---- un-fused attention entry point ---------------------------------------------
+
+WS = 0x60000000
+
+
+def _unf(dtype=0, **over):
+    a = dict(GOOD, ws=WS, ws_bytes=1 << 30)
+    a.update(over)
+    lib = attn.load_library()
+    return lib.attn_fwd_unfused(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["ws_bytes"], a["B"], a["H"],
+                                a["N"], a["d"], a["causal"], a["scale"], None, dtype)
+
+
+def test_unfused_workspace_bytes():
+    lib = attn.load_library()
+    assert lib.attn_unfused_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 100 * 4
+    assert lib.attn_unfused_workspace_bytes(1, 65535, 1) == 65535 * 4
+    assert lib.attn_unfused_workspace_bytes(1, 65536, 1) == 0          # B*H beyond one grid dimension
+    assert lib.attn_unfused_workspace_bytes(1, 1 << 14, 1 << 17) == 0  # B*H*N rows beyond an int
+    assert lib.attn_unfused_workspace_bytes(0, 3, 100) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(B=1, H=65536), 2), (dict(B=1 << 14, H=1, N=1 << 17), 2),
+    (dict(d=96), 3), (dict(q=Q + 8), 4), (dict(scale=math.nan), 7), (dict(causal=3), 8),
+    (dict(ws=0), 11), (dict(ws=WS + 4), 11), (dict(ws_bytes=2 * 3 * 100 * 100 * 4 - 1), 11),
+    (dict(ws=O), 9), (dict(ws=V - 16), 9),
+])
+def test_unfused_rejects_invalid_arguments(over, code):
+    assert _unf(**over) == code
+    assert _unf(dtype=1, **over) == code
+
+
+def test_unfused_rejects_unknown_dtype():
+    assert _unf(dtype=2) == 5

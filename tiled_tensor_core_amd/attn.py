@@ -48,6 +48,7 @@ STATUS = {
     8: "ATTN_ERR_CAUSAL",
     9: "ATTN_ERR_ALIAS",
     10: "ATTN_ERR_CONFIG",
+    11: "ATTN_ERR_WORKSPACE",
 }
 
 ATTN_PRIO_DEFAULT = 0
@@ -77,7 +78,8 @@ GEMM_EPI_BIAS = 1
 GEMM_EPI_BIAS_GELU = 2
 
 EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg", "attn_resolve_cfg",
-           "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows", "gemm_bf16"]
+           "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows", "gemm_bf16",
+           "attn_fwd_unfused", "attn_unfused_workspace_bytes"]
 
 
 class AttnError(RuntimeError):
@@ -123,6 +125,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gemm_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.gemm_bf16.restype = ctypes.c_int
+    lib.attn_fwd_unfused.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_ulonglong] + [ctypes.c_int] * 5 +
+                                     [ctypes.c_float, ctypes.c_void_p, ctypes.c_int])
+    lib.attn_fwd_unfused.restype = ctypes.c_int
+    lib.attn_unfused_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    lib.attn_unfused_workspace_bytes.restype = ctypes.c_ulonglong
     _lib = lib
     return lib
 
@@ -230,6 +237,46 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None
         raise TypeError("dtype is required when q is a raw address")
     code = _dtype_code(q, dtype)
     _check(lib.attn_fwd(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code), code))
+
+
+def attn_unfused_workspace_bytes(B, H, N) -> int:
+    """Workspace bytes attn_fwd_unfused needs (0 if the shape is outside its limits)."""
+    return int(load_library().attn_unfused_workspace_bytes(int(B), int(H), int(N)))
+
+
+def attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, causal, scale, stream=None,
+                     dtype=None) -> None:
+    """Enqueue the un-fused attention forward (see include/attn.h): scores into
+    ``workspace``, row softmax in place, then P V."""
+    lib = load_library()
+    if dtype is None and isinstance(q, int):
+        raise TypeError("dtype is required when q is a raw address")
+    code = _dtype_code(q, dtype)
+    if _is_tensor(workspace):
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        have = workspace.numel() * workspace.element_size()
+        if int(workspace_bytes) > have:
+            raise ValueError(f"workspace_bytes {workspace_bytes} exceeds the tensor's {have} bytes")
+    args = _args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code)
+    _check(lib.attn_fwd_unfused(*args[:5], _ptr(workspace), int(workspace_bytes), *args[5:], code))
+
+
+def fwd_unfused(q, k, v, causal: bool, scale: float, stream=None):
+    """O (fp32) and LSE (fp32) by the un-fused path, allocating its workspace with torch."""
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
+    B, H, N, d = q.shape
+    need = attn_unfused_workspace_bytes(B, H, N)
+    if need == 0:
+        raise ValueError(f"B={B}, H={H}, N={N} is outside the un-fused path's limits")
+    ws = torch.empty((need // 4,), dtype=torch.float32, device=q.device)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    attn_fwd_unfused(q, k, v, o, lse, ws, need, B, H, N, d, bool(causal), scale, stream)
+    return o, lse
 
 
 def _cfg(cfg) -> LaunchCfg | None:

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "softmax_kernel.hip"),
-           os.path.join(CSRC, "gemm_kernel.hip"),
+           os.path.join(CSRC, "gemm_kernel.hip"), os.path.join(CSRC, "unfused_kernel.hip"),
            os.path.join(CSRC, "attn_api.cpp")]
 
 HIPCC_FLAGS = [

@@ -13,6 +13,7 @@
 #include "attn_launch.h"
 #include "gemm_launch.h"
 #include "softmax_launch.h"
+#include "unfused_launch.h"
 
 namespace {
 
@@ -111,6 +112,56 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   return ATTN_OK;
 }
 
+// Shapes the un-fused path takes: attn_fwd's, with B*H in one grid
+// dimension (<= 65535) and B*H*N softmax rows in an int.
+bool unfused_shape_ok(int B, int H, int N, int d) {
+  if (!shape_ok(B, H, N, d)) return false;
+  const long long bh = (long long)B * H;
+  return bh <= 65535 && bh * N < (1LL << 31);
+}
+
+unsigned long long unfused_ws_bytes(int B, int H, int N) {
+  return (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)N * 4ull;
+}
+
+int run_unfused(const void* q, const void* k, const void* v, float* o, float* lse, void* ws,
+                unsigned long long ws_bytes, int B, int H, int N, int d, int causal, float scale, void* stream,
+                int dtype) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+  if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!unfused_shape_ok(B, H, N, d)) return ATTN_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse)) return ATTN_ERR_ALIGN;
+  const unsigned long long need = unfused_ws_bytes(B, H, N);
+  if (!ws || misaligned(ws) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  const long long rows = (long long)B * H * N;
+  const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4, lse_bytes = (size_t)rows * 4;
+  if (overlaps(o, o_bytes, lse, lse_bytes) || overlaps(o, o_bytes, q, in_bytes) ||
+      overlaps(o, o_bytes, k, in_bytes) || overlaps(o, o_bytes, v, in_bytes) ||
+      overlaps(lse, lse_bytes, q, in_bytes) || overlaps(lse, lse_bytes, k, in_bytes) ||
+      overlaps(lse, lse_bytes, v, in_bytes) || overlaps(ws, need, q, in_bytes) || overlaps(ws, need, k, in_bytes) ||
+      overlaps(ws, need, v, in_bytes) || overlaps(ws, need, o, o_bytes) || overlaps(ws, need, lse, lse_bytes))
+    return ATTN_ERR_ALIAS;
+  ttc_unf::UnfParams prm{};
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k = static_cast<const uint16_t*>(k);
+  prm.v = static_cast<const uint16_t*>(v);
+  prm.s = static_cast<float*>(ws);
+  prm.o = o;
+  prm.N = N;
+  prm.scale = scale;
+  const hipError_t e = ttc_unf::launch_unfused(dtype == ATTN_BF16, d, causal == 1, prm, B * H, lse,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 int run_softmax(const void* x, void* y, int rows, int cols, int dtype, void* stream) {
   if (dtype != SOFTMAX_F32 && dtype != SOFTMAX_BF16 && dtype != SOFTMAX_FP16) return ATTN_ERR_DTYPE;
   if (!x || !y) return ATTN_ERR_NULL;
@@ -121,7 +172,7 @@ int run_softmax(const void* x, void* y, int rows, int cols, int dtype, void* str
   const long long bytes = (long long)rows * cols * esize;
   if (misaligned(x) || misaligned(y)) return ATTN_ERR_ALIGN;
   if (x != y && overlaps(x, (size_t)bytes, y, (size_t)bytes)) return ATTN_ERR_ALIAS;
-  hipError_t e = ttc_sm::launch_softmax(dtype, x, y, rows, cols, static_cast<hipStream_t>(stream));
+  hipError_t e = ttc_sm::launch_softmax(dtype, x, y, rows, cols, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = hipGetErrorString(e);
     return ATTN_ERR_HIP;
@@ -164,6 +215,17 @@ extern "C" {
 int gemm_bf16(const void* a, const void* w, const float* bias, void* c, int M, int N, int K, int epilogue,
               void* stream) {
   return run_gemm(a, w, bias, c, M, N, K, epilogue, stream);
+}
+
+int attn_fwd_unfused(const void* q, const void* k, const void* v, float* o, float* lse, void* workspace,
+                     unsigned long long workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+                     void* stream, int dtype) {
+  return run_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, causal, scale, stream, dtype);
+}
+
+unsigned long long attn_unfused_workspace_bytes(int B, int H, int N) {
+  if (!unfused_shape_ok(B, H, N, 64)) return 0;
+  return unfused_ws_bytes(B, H, N);
 }
 
 int softmax_rows(const void* x, void* y, int rows, int cols, int dtype, void* stream) {
@@ -230,6 +292,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_CAUSAL: return "causal must be 0 or 1";
     case ATTN_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
     case ATTN_ERR_CONFIG: return "launch configuration field out of range";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than the shape needs";
     default: return "unknown status";
   }
 }

@@ -116,6 +116,12 @@ SM_INLINE float shift(float cm, float cn) {
   return ex2(cm - cn);
 }
 
+// Natural log-sum-exp of a row from its offset c(m) and its sum s against
+// that offset: sum_j e^x_j = 2^(c(m)) * s.
+SM_INLINE float row_lse(float cm, float s) {
+  return (cm + __builtin_amdgcn_logf(s)) * 0.69314718055994530942f;
+}
+
 // Running (maximum, sum) of one lane, the sum taken against offset(m): merge
 // a block maximum mb and block sum sb taken against offset(mb).  A side with
 // no element yet has m = -inf, s = 0.
@@ -130,7 +136,7 @@ SM_INLINE void merge(float& m, float& s, float mb, float sb) {
 
 // Rows of at most NCH * 1 KiB whose byte length is a multiple of 16.
 template <int T, int NCH>
-__global__ void __launch_bounds__(kWaves * 64) softmax_reg(const uint8_t* x, uint8_t* y, int rows, int row_bytes) {
+__global__ void __launch_bounds__(kWaves * 64) softmax_reg(const uint8_t* x, uint8_t* y, int rows, int row_bytes, float* lse) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
@@ -163,6 +169,7 @@ __global__ void __launch_bounds__(kWaves * 64) softmax_reg(const uint8_t* x, uin
     }
     s = wave_sum(s);
     const float inv = 1.0f / s;
+    if (lse && lane == 0) lse[r] = row_lse(mc, s);
     const __amdgpu_buffer_rsrc_t ys = rsrc(y + roff, (uint32_t)row_bytes);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -207,7 +214,7 @@ constexpr int kBlkChunks = T == 0 ? kMaxChunks : kMaxChunks / 2;
 // c * kBlockWaves + w (c < NCH) of the row in registers, so the row is read
 // once; the row's maximum and sum combine across the waves through LDS.
 template <int T, int NCH>
-__global__ void __launch_bounds__(kBlockWaves * 64) softmax_blk(const uint8_t* x, uint8_t* y, int rows, int row_bytes) {
+__global__ void __launch_bounds__(kBlockWaves * 64) softmax_blk(const uint8_t* x, uint8_t* y, int rows, int row_bytes, float* lse) {
   using E = Elem<T>;
   __shared__ float red_max[kBlockWaves], red_sum[kBlockWaves];
   const int lane = threadIdx.x & 63;
@@ -238,7 +245,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) softmax_blk(const uint8_t* x
 #pragma unroll
         for (int k = 0; k < E::kPerWord; ++k) s += ex2(__builtin_fmaf(E::get(v[c][w], k), kLog2e, -mc));
     }
-    const float inv = 1.0f / block_reduce(s, red_sum, false);
+    const float tot = block_reduce(s, red_sum, false);
+    const float inv = 1.0f / tot;
+    if (lse && threadIdx.x == 0) lse[r] = row_lse(mc, tot);
     const __amdgpu_buffer_rsrc_t ys = rsrc(y + roff, (uint32_t)row_bytes);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -259,7 +268,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) softmax_blk(const uint8_t* x
 // kMaxChunks KiB.  The first pass keeps a running (maximum, sum) per lane;
 // the lanes' pairs combine across the workgroup; the second pass writes.
 template <int T>
-__global__ void __launch_bounds__(kBlockWaves * 64) softmax_seg(const uint8_t* x, uint8_t* y, int rows, int row_bytes) {
+__global__ void __launch_bounds__(kBlockWaves * 64) softmax_seg(const uint8_t* x, uint8_t* y, int rows, int row_bytes, float* lse) {
   using E = Elem<T>;
   constexpr int SEG = kBlockWaves * kMaxChunks * 1024;
   __shared__ float red_max[kBlockWaves], red_sum[kBlockWaves];
@@ -300,7 +309,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) softmax_seg(const uint8_t* x
     }
     const float M = block_reduce(m, red_max, true);
     const float mc = offset(M);
-    const float inv = 1.0f / block_reduce((m == -INFINITY) ? 0.0f : s * shift(offset(m), mc), red_sum, false);
+    const float tot = block_reduce((m == -INFINITY) ? 0.0f : s * shift(offset(m), mc), red_sum, false);
+    const float inv = 1.0f / tot;
+    if (lse && threadIdx.x == 0) lse[r] = row_lse(mc, tot);
     for (int seg = 0; seg < row_bytes; seg += SEG) {
       const __amdgpu_buffer_rsrc_t xs = rsrc(x + roff + seg, (uint32_t)(row_bytes - seg));
       const __amdgpu_buffer_rsrc_t ys = rsrc(y + roff + seg, (uint32_t)(row_bytes - seg));
@@ -326,7 +337,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) softmax_seg(const uint8_t* x
 // reading the row again.  Used when a row's byte length is not a multiple of
 // 16, so 16-byte loads do not apply.
 template <int T>
-__global__ void __launch_bounds__(kWaves * 64) softmax_elem(const uint8_t* x, uint8_t* y, int rows, int cols) {
+__global__ void __launch_bounds__(kWaves * 64) softmax_elem(const uint8_t* x, uint8_t* y, int rows, int cols, float* lse) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
@@ -342,7 +353,9 @@ __global__ void __launch_bounds__(kWaves * 64) softmax_elem(const uint8_t* x, ui
     const float mc = offset(wave_max(m));
     float s = 0.0f;
     for (int j = lane; j < cols; j += 64) s += ex2(__builtin_fmaf(load(j), kLog2e, -mc));
-    const float inv = 1.0f / wave_sum(s);
+    const float tot = wave_sum(s);
+    const float inv = 1.0f / tot;
+    if (lse && lane == 0) lse[r] = row_lse(mc, tot);
     for (int j = lane; j < cols; j += 64) {
       const float p = ex2(__builtin_fmaf(load(j), kLog2e, -mc)) * inv;
       // plain stores: the caches merge the lanes' partial lines before they
@@ -380,13 +393,13 @@ static int grid_blocks(int rows) {
 }
 
 template <int T>
-static hipError_t launch_t(const void* x, void* y, int rows, int cols, hipStream_t stream) {
+static hipError_t launch_t(const void* x, void* y, int rows, int cols, float* lse, hipStream_t stream) {
   const long long row_bytes = (long long)cols * Elem<T>::kBytes;
   const dim3 block(kWaves * 64);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* yb = static_cast<uint8_t*>(y);
   if (row_bytes % 16 != 0) {
-    hipLaunchKernelGGL(softmax_elem<T>, dim3(grid_for(rows)), block, 0, stream, xb, yb, rows, cols);
+    hipLaunchKernelGGL(softmax_elem<T>, dim3(grid_for(rows)), block, 0, stream, xb, yb, rows, cols, lse);
     return hipGetLastError();
   }
   const int rb = (int)row_bytes;
@@ -394,15 +407,15 @@ static hipError_t launch_t(const void* x, void* y, int rows, int cols, hipStream
   if (pieces <= kMaxChunks) {
     const dim3 grid(grid_for(rows));
     if (pieces <= 1)
-      hipLaunchKernelGGL((softmax_reg<T, 1>), grid, block, 0, stream, xb, yb, rows, rb);
+      hipLaunchKernelGGL((softmax_reg<T, 1>), grid, block, 0, stream, xb, yb, rows, rb, lse);
     else if (pieces <= 2)
-      hipLaunchKernelGGL((softmax_reg<T, 2>), grid, block, 0, stream, xb, yb, rows, rb);
+      hipLaunchKernelGGL((softmax_reg<T, 2>), grid, block, 0, stream, xb, yb, rows, rb, lse);
     else if (pieces <= 4)
-      hipLaunchKernelGGL((softmax_reg<T, 4>), grid, block, 0, stream, xb, yb, rows, rb);
+      hipLaunchKernelGGL((softmax_reg<T, 4>), grid, block, 0, stream, xb, yb, rows, rb, lse);
     else if (pieces <= 8)
-      hipLaunchKernelGGL((softmax_reg<T, 8>), grid, block, 0, stream, xb, yb, rows, rb);
+      hipLaunchKernelGGL((softmax_reg<T, 8>), grid, block, 0, stream, xb, yb, rows, rb, lse);
     else
-      hipLaunchKernelGGL((softmax_reg<T, kMaxChunks>), grid, block, 0, stream, xb, yb, rows, rb);
+      hipLaunchKernelGGL((softmax_reg<T, kMaxChunks>), grid, block, 0, stream, xb, yb, rows, rb, lse);
     return hipGetLastError();
   }
   // one row per workgroup of kBlockWaves waves
@@ -410,23 +423,23 @@ static hipError_t launch_t(const void* x, void* y, int rows, int cols, hipStream
   const dim3 bgrid(grid_blocks(rows));
   const int per_wave = (pieces + kBlockWaves - 1) / kBlockWaves;
   if (per_wave <= 2)
-    hipLaunchKernelGGL((softmax_blk<T, 2>), bgrid, bblock, 0, stream, xb, yb, rows, rb);
+    hipLaunchKernelGGL((softmax_blk<T, 2>), bgrid, bblock, 0, stream, xb, yb, rows, rb, lse);
   else if (per_wave <= 4)
-    hipLaunchKernelGGL((softmax_blk<T, 4>), bgrid, bblock, 0, stream, xb, yb, rows, rb);
+    hipLaunchKernelGGL((softmax_blk<T, 4>), bgrid, bblock, 0, stream, xb, yb, rows, rb, lse);
   else if (per_wave <= 8)
-    hipLaunchKernelGGL((softmax_blk<T, 8>), bgrid, bblock, 0, stream, xb, yb, rows, rb);
+    hipLaunchKernelGGL((softmax_blk<T, 8>), bgrid, bblock, 0, stream, xb, yb, rows, rb, lse);
   else if (per_wave <= kBlkChunks<T>)
-    hipLaunchKernelGGL((softmax_blk<T, kBlkChunks<T>>), bgrid, bblock, 0, stream, xb, yb, rows, rb);
+    hipLaunchKernelGGL((softmax_blk<T, kBlkChunks<T>>), bgrid, bblock, 0, stream, xb, yb, rows, rb, lse);
   else
-    hipLaunchKernelGGL(softmax_seg<T>, bgrid, bblock, 0, stream, xb, yb, rows, rb);
+    hipLaunchKernelGGL(softmax_seg<T>, bgrid, bblock, 0, stream, xb, yb, rows, rb, lse);
   return hipGetLastError();
 }
 
-hipError_t launch_softmax(int dtype, const void* x, void* y, int rows, int cols, hipStream_t stream) {
+hipError_t launch_softmax(int dtype, const void* x, void* y, int rows, int cols, float* lse, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_t<0>(x, y, rows, cols, stream);
-    case 1: return launch_t<1>(x, y, rows, cols, stream);
-    default: return launch_t<2>(x, y, rows, cols, stream);
+    case 0: return launch_t<0>(x, y, rows, cols, lse, stream);
+    case 1: return launch_t<1>(x, y, rows, cols, lse, stream);
+    default: return launch_t<2>(x, y, rows, cols, lse, stream);
   }
 }
 
