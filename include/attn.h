@@ -66,7 +66,8 @@ enum attn_status {
   ATTN_ERR_CAUSAL = 8,         /* causal is not 0 or 1                           */
   ATTN_ERR_ALIAS = 9,          /* o or lse overlaps another buffer               */
   ATTN_ERR_CONFIG = 10,        /* a launch configuration field is out of range   */
-  ATTN_ERR_WORKSPACE = 11      /* workspace NULL, too small or misaligned        */
+  ATTN_ERR_WORKSPACE = 11,     /* workspace NULL, too small or misaligned        */
+  ATTN_ERR_SCRATCH = 12        /* shape needs more than the built-in scratch     */
 };
 
 enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1 };
@@ -184,6 +185,22 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, float* o, floa
 /* Bytes of workspace attn_fwd_unfused needs: B*H*N*N*4 (0 if the shape is
  * outside its limits). */
 unsigned long long attn_unfused_workspace_bytes(int B, int H, int N);
+
+/* attn_fwd_unfused without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the score matrix goes to a fixed scratch
+ * buffer of ATTN_UNFUSED_SCRATCH_BYTES (64 MiB) inside the library, one per
+ * device, held from the first call until the process ends.  The call
+ * allocates nothing; it looks the buffer's address up once per device (on
+ * its first call there).  Shapes whose B*H*N*N*4 exceeds the buffer return
+ * ATTN_ERR_SCRATCH before any HIP call.  Every call on a device uses that
+ * device's one buffer and leaves its contents behind: calls that overlap on
+ * one device (other streams, other threads) race and give wrong results.
+ * Otherwise the same arguments, limits and errors as attn_fwd_unfused. */
+#define ATTN_UNFUSED_SCRATCH_BYTES (64ull << 20)
+int attn_fwd_unfused_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                             int B, int H, int N, int d, int causal, float scale, void* stream,
+                             int dtype);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* attn_status_str(int status);

@@ -337,3 +337,16 @@ def test_unfused_rejects_invalid_arguments(over, code):
 
 def test_unfused_rejects_unknown_dtype():
     assert _unf(dtype=2) == 5
+
+
+def test_unfused_noalloc_rejects_oversize_before_any_hip_call():
+    """B*H*N*N*4 above the 64 MiB scratch returns ATTN_ERR_SCRATCH; the host
+    checks run first (no GPU here)."""
+    lib = attn.load_library()
+    args = (Q, K, V, O, L)
+    # 1 x 16 x 1024: exactly 64 MiB of scores fits; one more row does not
+    assert lib.attn_fwd_unfused_noalloc(*args, 1, 16, 1025, 64, 0, 0.125, None, 0) == 12
+    assert lib.attn_fwd_unfused_noalloc(*args, 4, 16, 1024, 64, 1, 0.125, None, 1) == 12
+    assert lib.attn_fwd_unfused_noalloc(*args, 1, 16, 1024, 96, 0, 0.125, None, 0) == 3
+    assert lib.attn_fwd_unfused_noalloc(Q + 8, K, V, O, L, 1, 2, 64, 64, 0, 0.125, None, 0) == 4
+    assert attn.attn_status_str(12) != "unknown status"

@@ -49,6 +49,7 @@ STATUS = {
     9: "ATTN_ERR_ALIAS",
     10: "ATTN_ERR_CONFIG",
     11: "ATTN_ERR_WORKSPACE",
+    12: "ATTN_ERR_SCRATCH",
 }
 
 ATTN_PRIO_DEFAULT = 0
@@ -79,7 +80,9 @@ GEMM_EPI_BIAS_GELU = 2
 
 EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg", "attn_resolve_cfg",
            "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows", "gemm_bf16",
-           "attn_fwd_unfused", "attn_unfused_workspace_bytes"]
+           "attn_fwd_unfused", "attn_unfused_workspace_bytes", "attn_fwd_unfused_noalloc"]
+
+ATTN_UNFUSED_SCRATCH_BYTES = 64 << 20
 
 
 class AttnError(RuntimeError):
@@ -128,6 +131,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_unfused.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_ulonglong] + [ctypes.c_int] * 5 +
                                      [ctypes.c_float, ctypes.c_void_p, ctypes.c_int])
     lib.attn_fwd_unfused.restype = ctypes.c_int
+    lib.attn_fwd_unfused_noalloc.argtypes = fwd_args + [ctypes.c_int]
+    lib.attn_fwd_unfused_noalloc.restype = ctypes.c_int
     lib.attn_unfused_workspace_bytes.argtypes = [ctypes.c_int] * 3
     lib.attn_unfused_workspace_bytes.restype = ctypes.c_ulonglong
     _lib = lib
@@ -260,6 +265,16 @@ def attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, ca
             raise ValueError(f"workspace_bytes {workspace_bytes} exceeds the tensor's {have} bytes")
     args = _args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code)
     _check(lib.attn_fwd_unfused(*args[:5], _ptr(workspace), int(workspace_bytes), *args[5:], code))
+
+
+def attn_fwd_unfused_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, dtype=None) -> None:
+    """attn_fwd_unfused with the library's fixed scratch for the scores (see
+    include/attn.h): allocates nothing; B*H*N*N*4 <= ATTN_UNFUSED_SCRATCH_BYTES."""
+    lib = load_library()
+    if dtype is None and isinstance(q, int):
+        raise TypeError("dtype is required when q is a raw address")
+    code = _dtype_code(q, dtype)
+    _check(lib.attn_fwd_unfused_noalloc(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, code), code))
 
 
 def fwd_unfused(q, k, v, causal: bool, scale: float, stream=None):

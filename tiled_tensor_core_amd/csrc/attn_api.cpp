@@ -124,9 +124,11 @@ unsigned long long unfused_ws_bytes(int B, int H, int N) {
   return (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)N * 4ull;
 }
 
+// ws == nullptr with ws_bytes == 0 and use_scratch: the library's scratch
+// (looked up after every host check has passed).
 int run_unfused(const void* q, const void* k, const void* v, float* o, float* lse, void* ws,
                 unsigned long long ws_bytes, int B, int H, int N, int d, int causal, float scale, void* stream,
-                int dtype) {
+                int dtype, bool use_scratch = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
@@ -136,7 +138,11 @@ int run_unfused(const void* q, const void* k, const void* v, float* o, float* ls
   if (!unfused_shape_ok(B, H, N, d)) return ATTN_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse)) return ATTN_ERR_ALIGN;
   const unsigned long long need = unfused_ws_bytes(B, H, N);
-  if (!ws || misaligned(ws) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (need > ttc_unf::kScratchBytes) return ATTN_ERR_SCRATCH;
+  } else if (!ws || misaligned(ws) || ws_bytes < need) {
+    return ATTN_ERR_WORKSPACE;
+  }
   const long long rows = (long long)B * H * N;
   const size_t in_bytes = (size_t)rows * d * 2, o_bytes = (size_t)rows * d * 4, lse_bytes = (size_t)rows * 4;
   if (overlaps(o, o_bytes, lse, lse_bytes) || overlaps(o, o_bytes, q, in_bytes) ||
@@ -145,6 +151,13 @@ int run_unfused(const void* q, const void* k, const void* v, float* o, float* ls
       overlaps(lse, lse_bytes, v, in_bytes) || overlaps(ws, need, q, in_bytes) || overlaps(ws, need, k, in_bytes) ||
       overlaps(ws, need, v, in_bytes) || overlaps(ws, need, o, o_bytes) || overlaps(ws, need, lse, lse_bytes))
     return ATTN_ERR_ALIAS;
+  if (use_scratch) {
+    const hipError_t se = ttc_unf::scratch_address(&ws);
+    if (se != hipSuccess) {
+      g_last_error = hipGetErrorString(se);
+      return ATTN_ERR_HIP;
+    }
+  }
   ttc_unf::UnfParams prm{};
   prm.q = static_cast<const uint16_t*>(q);
   prm.k = static_cast<const uint16_t*>(k);
@@ -223,6 +236,11 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, float* o, floa
   return run_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, causal, scale, stream, dtype);
 }
 
+int attn_fwd_unfused_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N,
+                             int d, int causal, float scale, void* stream, int dtype) {
+  return run_unfused(q, k, v, o, lse, nullptr, 0, B, H, N, d, causal, scale, stream, dtype, true);
+}
+
 unsigned long long attn_unfused_workspace_bytes(int B, int H, int N) {
   if (!unfused_shape_ok(B, H, N, 64)) return 0;
   return unfused_ws_bytes(B, H, N);
@@ -293,6 +311,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
     case ATTN_ERR_CONFIG: return "launch configuration field out of range";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than the shape needs";
+    case ATTN_ERR_SCRATCH: return "B*H*N*N*4 exceeds the built-in scratch (ATTN_UNFUSED_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "softmax_launch.h"
 #include "unfused_launch.h"
 
@@ -266,6 +268,35 @@ hipError_t launch_unfused(bool bf16, int d, bool causal, const UnfParams& prm, i
   }
   if (d == 64) return causal ? launch_t<false, 64, true>(prm, BH, lse, stream) : launch_t<false, 64, false>(prm, BH, lse, stream);
   return causal ? launch_t<false, 128, true>(prm, BH, lse, stream) : launch_t<false, 128, false>(prm, BH, lse, stream);
+}
+
+// ---- the scratch of the allocation-free entry point ----------------------------
+// A fixed-size score buffer in the library's own device memory, for callers
+// that cannot allocate.  Every device the library runs on holds one copy
+// until the process ends.  In host code `scratch` only stands for the symbol:
+// its device address, different on each device, comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / 4];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace ttc_unf

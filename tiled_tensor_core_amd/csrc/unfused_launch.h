@@ -16,6 +16,14 @@ struct UnfParams {
   float scale;         // multiplier of the scores
 };
 
+// Bytes of the device scratch the allocation-free entry point uses for the
+// score matrix (B*H*N*N*4 must not exceed it).
+constexpr unsigned long long kScratchBytes = 64ull << 20;
+
+// Device address of that scratch on the current device (looked up on the
+// first call per device, then cached).
+hipError_t scratch_address(void** out);
+
 // Enqueue scores -> row softmax (writing lse) -> P V on `stream`.
 // Arguments are already validated (BH <= 65535, BH * N < 2^31).
 hipError_t launch_unfused(bool bf16, int d, bool causal, const UnfParams& prm, int BH, float* lse,
