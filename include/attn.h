@@ -109,11 +109,13 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
  *
  *   mode    the exponent reference of the online softmax (attn_ref_mode
  *           below).
+ *   tile    the tile variant (attn_tile below).
  *
  * A field of 0 (ATTN_PRIO_DEFAULT for prio) takes the built-in choice.  The
- * fields other than mode change only which workgroup computes which (head,
- * query block) item and in what order, never an item's arithmetic: every
- * valid configuration of one mode gives bit-identical o and lse. */
+ * fields other than mode and tile change only which workgroup computes which
+ * (head, query block) item and in what order, never an item's arithmetic:
+ * every valid configuration of one (mode, tile) gives bit-identical o and
+ * lse.  Different modes and tiles differ in rounding only. */
 #define ATTN_MAX_WORKGROUPS (1 << 20)
 enum attn_prio { ATTN_PRIO_DEFAULT = 0, ATTN_PRIO_ON = 1, ATTN_PRIO_OFF = 2 };
 
@@ -136,13 +138,41 @@ enum attn_prio { ATTN_PRIO_DEFAULT = 0, ATTN_PRIO_ON = 1, ATTN_PRIO_OFF = 2 };
  *                     outgrows it by 2^2 (bf16) or 2^8 (fp16). */
 enum attn_ref_mode { ATTN_REF_DEFAULT = 0, ATTN_REF_FIXED = 1, ATTN_REF_RUNNING = 2 };
 
+/* Tile variant (the `tile` field): query rows per work item and waves per
+ * workgroup.
+ *   ATTN_TILE_128  128 rows, 4 waves of 32 rows, two workgroups per compute
+ *                  unit.  The built-in choice.
+ *   ATTN_TILE_256  256 rows, 8 waves, one workgroup per compute unit: each
+ *                  K/V tile brought into LDS serves twice the rows, at the
+ *                  price of wider causal diagonals and 8-wave barriers.
+ *                  ATTN_REF_FIXED mode only. */
+enum attn_tile { ATTN_TILE_DEFAULT = 0, ATTN_TILE_128 = 1, ATTN_TILE_256 = 2 };
+
 typedef struct attn_launch_cfg {
   int n_dom;
   int n_work;
   int grp;
   int prio;
   int mode;   /* attn_ref_mode */
+  int tile;   /* attn_tile */
 } attn_launch_cfg;
+
+/* Compiled resources of one kernel variant, as the device reports them. */
+typedef struct attn_tile_resources {
+  int rows;            /* query rows per work item                          */
+  int waves;           /* waves per workgroup                               */
+  int vgprs;           /* vector registers per lane                         */
+  int lds_bytes;       /* static LDS per workgroup                          */
+  int scratch_bytes;   /* scratch (spilled registers) per lane; 0 by design */
+  int groups_per_cu;   /* workgroups a compute unit runs at once            */
+} attn_tile_resources;
+
+/* Resources of the kernel attn_fwd_cfg runs for (tile, mode, dtype, d,
+ * causal) on the current device (fields of 0 mean the built-in choice), so
+ * a search can drop variants that spill or exceed the LDS.  Queries the
+ * device; enqueues nothing.  Errors: ATTN_ERR_NULL, _DTYPE, _UNSUPPORTED_D,
+ * _CAUSAL, _CONFIG (no such variant), _HIP (query failed). */
+int attn_tile_info(int tile, int mode, int dtype, int d, int causal, attn_tile_resources* out);
 
 /* attn_fwd with an explicit launch configuration; cfg NULL is attn_fwd.
  * The caller owns cfg; it is read during the call only.  A field out of

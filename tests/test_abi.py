@@ -147,6 +147,7 @@ def test_softmax_rejects_invalid_arguments(over, code):
 BAD_CFGS = [  # (n_dom, n_work, grp, prio)
     (2, 0, 0, 0), (-1, 0, 0, 0), (16, 0, 0, 0), (0, -1, 0, 0), (0, (1 << 20) + 1, 0, 0),
     (0, 0, -3, 0), (0, 0, 0, 3), (0, 0, 0, -1), (0, 0, 0, 0, 3), (0, 0, 0, 0, -1),
+    (0, 0, 0, 0, 0, 3), (0, 0, 0, 0, 0, -1), (0, 0, 0, 0, 2, 2),
 ]
 
 
@@ -179,9 +180,9 @@ def test_resolve_cfg_rejects_null():
 
 
 def test_cfg_forms():
-    assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1, 0)
-    assert attn._cfg((8, 64, 4, 1, 2)).as_tuple() == (8, 64, 4, 1, 2)
-    assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0, 0)
+    assert attn._cfg((8, 64, 4, 1)).as_tuple() == (8, 64, 4, 1, 0, 0)
+    assert attn._cfg((8, 64, 4, 1, 2)).as_tuple() == (8, 64, 4, 1, 2, 0)
+    assert attn._cfg({"n_work": 3}).as_tuple() == (0, 3, 0, 0, 0, 0)
     assert attn._cfg(None) is None
 
 

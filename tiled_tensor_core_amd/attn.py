@@ -58,6 +58,9 @@ ATTN_PRIO_OFF = 2
 ATTN_REF_DEFAULT = 0
 ATTN_REF_FIXED = 1
 ATTN_REF_RUNNING = 2
+ATTN_TILE_DEFAULT = 0
+ATTN_TILE_128 = 1
+ATTN_TILE_256 = 2
 ATTN_MAX_WORKGROUPS = 1 << 20
 
 
@@ -65,14 +68,24 @@ class LaunchCfg(ctypes.Structure):
     """attn_launch_cfg of include/attn.h (a field of 0 takes the built-in choice)."""
 
     _fields_ = [("n_dom", ctypes.c_int), ("n_work", ctypes.c_int), ("grp", ctypes.c_int),
-                ("prio", ctypes.c_int), ("mode", ctypes.c_int)]
+                ("prio", ctypes.c_int), ("mode", ctypes.c_int), ("tile", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.n_dom, self.n_work, self.grp, self.prio, self.mode)
+        return (self.n_dom, self.n_work, self.grp, self.prio, self.mode, self.tile)
 
     def __repr__(self):
         return (f"LaunchCfg(n_dom={self.n_dom}, n_work={self.n_work}, grp={self.grp}, prio={self.prio}, "
-                f"mode={self.mode})")
+                f"mode={self.mode}, tile={self.tile})")
+
+
+class TileResources(ctypes.Structure):
+    """attn_tile_resources of include/attn.h."""
+
+    _fields_ = [(n, ctypes.c_int) for n in ("rows", "waves", "vgprs", "lds_bytes", "scratch_bytes",
+                                            "groups_per_cu")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 GEMM_EPI_NONE = 0
 GEMM_EPI_BIAS = 1
@@ -80,7 +93,7 @@ GEMM_EPI_BIAS_GELU = 2
 
 EXPORTS = ["attn_fwd", "attn_fwd_bf16", "attn_fwd_fp16", "attn_fwd_cfg", "attn_resolve_cfg",
            "attn_status_str", "attn_last_error", "attn_block_rows", "softmax_rows", "gemm_bf16",
-           "attn_fwd_unfused", "attn_unfused_workspace_bytes", "attn_fwd_unfused_noalloc"]
+           "attn_fwd_unfused", "attn_unfused_workspace_bytes", "attn_fwd_unfused_noalloc", "attn_tile_info"]
 
 ATTN_UNFUSED_SCRATCH_BYTES = 64 << 20
 
@@ -131,6 +144,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_unfused.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_ulonglong] + [ctypes.c_int] * 5 +
                                      [ctypes.c_float, ctypes.c_void_p, ctypes.c_int])
     lib.attn_fwd_unfused.restype = ctypes.c_int
+    lib.attn_tile_info.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(TileResources)]
+    lib.attn_tile_info.restype = ctypes.c_int
     lib.attn_fwd_unfused_noalloc.argtypes = fwd_args + [ctypes.c_int]
     lib.attn_fwd_unfused_noalloc.restype = ctypes.c_int
     lib.attn_unfused_workspace_bytes.argtypes = [ctypes.c_int] * 3
@@ -330,6 +345,13 @@ def attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> No
 def attn_fwd_fp16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
     lib = load_library()
     _check(lib.attn_fwd_fp16(*_args(q, k, v, o, lse, B, H, N, d, causal, scale, stream, ATTN_FP16)))
+
+
+def attn_tile_info(tile, mode, dtype, d, causal) -> dict:
+    """Compiled resources of a kernel variant on the current device (see include/attn.h)."""
+    r = TileResources()
+    _check(load_library().attn_tile_info(int(tile), int(mode), int(dtype), int(d), int(causal), ctypes.byref(r)))
+    return r.as_dict()
 
 
 def attn_status_str(code: int) -> str:

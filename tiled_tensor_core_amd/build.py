@@ -50,24 +50,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(isa_dir: str | None = None, verbose: bool = False) -> str:
-    """Compile every HIP source into the in-tree shared library; return its path."""
+def _compile(src: str, obj: str, isa_dir: str | None) -> subprocess.CompletedProcess:
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    cmd = [hipcc(), *flags, "-c", src, "-o", obj]
+    if isa_dir:
+        cmd.insert(1, "--save-temps")
+    return subprocess.run(cmd, cwd=isa_dir, capture_output=True, text=True)
+
+
+def build(isa_dir: str | None = None, verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source (in parallel, one hipcc per source) and link
+    the in-tree shared library; return its path."""
+    import concurrent.futures
+    import tempfile
+
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
-    cwd = None
     if isa_dir:
         os.makedirs(isa_dir, exist_ok=True)
-        cmd.insert(1, "--save-temps")
-        cwd = isa_dir
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
+    jobs = jobs or min(len(SOURCES), max(1, min(8, (os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="ttc_build_") as objdir:
+        objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
+        if verbose:
+            print(f"compiling {len(SOURCES)} sources with {jobs} jobs", flush=True)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda so: _compile(so[0], so[1], isa_dir), zip(SOURCES, objs)))
+        link = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                              capture_output=True, text=True)
+        results.append(link)
     noise = "is not a recognized feature for this target"
-    lines = [line for line in res.stderr.splitlines() if noise not in line]
+    lines = [line for r in results for line in r.stderr.splitlines() if noise not in line]
     report = [line for line in lines if "kernel-resource-usage" in line]
     err = "\n".join(line for line in lines if "kernel-resource-usage" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    failed = [r for r in results if r.returncode != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed ({failed[0].returncode}):\n{err}")
     # every kernel is designed to live in registers: scratch means spills or
     # a register array the compiler could not keep in registers
     kernel = None

@@ -47,6 +47,8 @@ bool cfg_valid(const attn_launch_cfg* c, long long bh) {
   if (c->grp < 0) return false;
   if (c->prio != ATTN_PRIO_DEFAULT && c->prio != ATTN_PRIO_ON && c->prio != ATTN_PRIO_OFF) return false;
   if (c->mode != ATTN_REF_DEFAULT && c->mode != ATTN_REF_FIXED && c->mode != ATTN_REF_RUNNING) return false;
+  if (c->tile != ATTN_TILE_DEFAULT && c->tile != ATTN_TILE_128 && c->tile != ATTN_TILE_256) return false;
+  if (c->tile == ATTN_TILE_256 && c->mode == ATTN_REF_RUNNING) return false;   // no such kernel
   return true;
 }
 
@@ -101,7 +103,7 @@ int run(const void* q, const void* k, const void* v, float* o, float* lse, int B
   }
 
   ttc::LaunchCfg cfg{};
-  if (user_cfg) cfg = {user_cfg->n_dom, user_cfg->n_work, user_cfg->grp, user_cfg->prio, user_cfg->mode};
+  if (user_cfg) cfg = {user_cfg->n_dom, user_cfg->n_work, user_cfg->grp, user_cfg->prio, user_cfg->mode, user_cfg->tile};
   hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, cfg);
   if (e == hipSuccess)
     e = ttc::launch_attn_fwd(dtype == ATTN_BF16, d, causal == 1, prm, cfg, static_cast<hipStream_t>(stream));
@@ -283,7 +285,7 @@ int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_lau
   ttc::AttnParams prm{};
   prm.BH = (int)bh;
   prm.N = N;
-  ttc::LaunchCfg c{cfg->n_dom, cfg->n_work, cfg->grp, cfg->prio, cfg->mode};
+  ttc::LaunchCfg c{cfg->n_dom, cfg->n_work, cfg->grp, cfg->prio, cfg->mode, cfg->tile};
   const hipError_t e = ttc::resolve_cfg(dtype == ATTN_BF16, d, causal == 1, prm, c);
   if (e != hipSuccess) {
     g_last_error = hipGetErrorString(e);
@@ -294,6 +296,7 @@ int attn_resolve_cfg(int B, int H, int N, int d, int causal, int dtype, attn_lau
   cfg->grp = c.grp;
   cfg->prio = c.prio;
   cfg->mode = c.mode;
+  cfg->tile = c.tile;
   return ATTN_OK;
 }
 
@@ -318,6 +321,29 @@ const char* attn_status_str(int status) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-int attn_block_rows(int d) { return (d == 64 || d == 128) ? ttc::block_rows(d) : 0; }
+int attn_block_rows(int d) { return (d == 64 || d == 128) ? ttc::block_rows(ATTN_TILE_128) : 0; }
+
+int attn_tile_info(int tile, int mode, int dtype, int d, int causal, attn_tile_resources* out) {
+  if (!out) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_D;
+  if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+  attn_launch_cfg c{0, 0, 0, 0, mode, tile};
+  if (!cfg_valid(&c, 8)) return ATTN_ERR_CONFIG;
+  ttc::KernelInfo k{};
+  const hipError_t e = ttc::kernel_info(dtype == ATTN_BF16, d, causal == 1, mode != ATTN_REF_RUNNING,
+                                        tile == 0 ? ATTN_TILE_128 : tile, k);
+  if (e != hipSuccess) {
+    g_last_error = hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+  }
+  out->rows = k.rows;
+  out->waves = k.waves;
+  out->vgprs = k.vgprs;
+  out->lds_bytes = k.lds_bytes;
+  out->scratch_bytes = k.scratch_bytes;
+  out->groups_per_cu = k.groups_per_cu;
+  return ATTN_OK;
+}
 
 }  // extern "C"

@@ -200,8 +200,6 @@ TTC_INLINE float max3(float a, float b, float c) {
 }
 
 constexpr int kBC = 64;        // keys per K/V tile
-constexpr int kNW = 4;         // waves per workgroup
-constexpr int kBM = kNW * 32;  // query rows per workgroup
 constexpr int kLead = 3;       // LDS operand reads issued this many MFMAs ahead
 constexpr int kChunks = 16;    // VALU slices per phase of a pipelined tile
 constexpr int kLoadEvery = 2;  // a pipelined tile issues one K/V tile load every this many steps
@@ -619,12 +617,15 @@ TTC_INLINE void store_b128(__amdgpu_buffer_rsrc_t rs, f32x4 v, unsigned voff) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)voff, 0, 2);
 }
 
-template <bool BF16, int D, bool CAUSAL, bool FIXED>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup, 32 query rows each: NW = 4 (128-row items, two
+// workgroups per compute unit) or 8 (256-row items, one workgroup per
+// compute unit, each K/V tile shared by twice the rows).
+template <bool BF16, int D, bool CAUSAL, bool FIXED, int NW>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
   using W = Wave<BF16, D, FIXED>;
   using S = Swz<D>;
-  constexpr int BC = kBC, NW = kNW, BM = kBM;
+  constexpr int BC = kBC, BM = NW * 32;
   constexpr int KB = W::KB, DK = W::DK, DT = W::DT;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int ROW_BYTES = D * 2;
@@ -646,7 +647,9 @@ attn_fwd_kernel(AttnParams p) {
   lds_u8* const V1 = (lds_u8*)v_lds1;
   // d = 64: a separate 16 KiB for turning O row-major before it is stored
   // (d = 128 uses the V buffer the last tile read; see the epilogue)
-  constexpr int STAGE_BYTES = D == 64 ? 4 * 4096 : 16;
+  // (8 waves need 32 KiB, more than a V buffer, for either head dim)
+  constexpr bool OWN_STAGE = D == 64 || NW != 4;
+  constexpr int STAGE_BYTES = OWN_STAGE ? NW * 4096 : 16;
   __shared__ __attribute__((aligned(1024))) uint8_t o_lds[STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -1110,7 +1113,7 @@ attn_fwd_kernel(AttnParams p) {
     // a wave whose rows all precede the tile's first key has nothing to do
     if (!CAUSAL || j * BC <= wr0 + 31) w.finish(sa, last_odd ? V1 : V0);
     if (more) load_q(bh2, qb2);   // the fragment registers are free from here on
-    if (D == 64) {
+    if (OWN_STAGE) {
       epilogue((lds_u8*)o_lds + wave * 4096);
     } else {
       // V buffer 1 takes the staging: when the last tile is even it held
@@ -1149,21 +1152,36 @@ attn_fwd_kernel(AttnParams p) {
 
 // ---- launch ------------------------------------------------------------------
 
-template <bool BF16, int D, bool CAUSAL, bool FIXED>
+template <bool BF16, int D, bool CAUSAL, bool FIXED, int NW>
 static const void* kernel_fn() {
-  return reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, FIXED>);
+  return reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, FIXED, NW>);
 }
 
-int block_rows(int d) {
-  (void)d;
-  return kBM;
+// Tile variants: 1 = 128-row items (4 waves), 2 = 256-row items (8 waves,
+// fixed-reference mode only).
+int block_rows(int tile) { return tile == 2 ? 256 : 128; }
+static int tile_waves(int tile) { return tile == 2 ? 8 : 4; }
+
+template <bool FIXED, int NW>
+static const void* variant_fn_m(bool bf16, int d, bool causal) {
+  return bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true, FIXED, NW>() : kernel_fn<true, 64, false, FIXED, NW>())
+                         : (causal ? kernel_fn<true, 128, true, FIXED, NW>() : kernel_fn<true, 128, false, FIXED, NW>()))
+              : (d == 64 ? (causal ? kernel_fn<false, 64, true, FIXED, NW>() : kernel_fn<false, 64, false, FIXED, NW>())
+                         : (causal ? kernel_fn<false, 128, true, FIXED, NW>() : kernel_fn<false, 128, false, FIXED, NW>()));
+}
+
+// The kernel of a (mode, tile) pair; the running-maximum mode exists for
+// the 128-row tile only (the launcher's callers check that).
+static const void* variant_fn(bool bf16, int d, bool causal, bool fixed, int tile) {
+  if (!fixed) return variant_fn_m<false, 4>(bf16, d, causal);
+  return tile == 2 ? variant_fn_m<true, 8>(bf16, d, causal) : variant_fn_m<true, 4>(bf16, d, causal);
 }
 
 // Workgroups of one kernel variant that the current device runs at once
 // (compute units x workgroups per compute unit), cached per device.
-static int resident_groups(int variant, const void* fn) {
+static int resident_groups(int variant, const void* fn, int threads) {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[16][kMaxDev];
+  static std::atomic<int> cache[32][kMaxDev];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (dev >= 0 && dev < kMaxDev) {
@@ -1172,31 +1190,38 @@ static int resident_groups(int variant, const void* fn) {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kNW * 64, 0) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess) return -1;
   const int n = std::max(1, cus) * std::max(1, per_cu);
   if (dev >= 0 && dev < kMaxDev) cache[variant][dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
-template <bool FIXED>
-static const void* variant_fn_m(bool bf16, int d, bool causal) {
-  return bf16 ? (d == 64 ? (causal ? kernel_fn<true, 64, true, FIXED>() : kernel_fn<true, 64, false, FIXED>())
-                         : (causal ? kernel_fn<true, 128, true, FIXED>() : kernel_fn<true, 128, false, FIXED>()))
-              : (d == 64 ? (causal ? kernel_fn<false, 64, true, FIXED>() : kernel_fn<false, 64, false, FIXED>())
-                         : (causal ? kernel_fn<false, 128, true, FIXED>() : kernel_fn<false, 128, false, FIXED>()));
-}
-
-static const void* variant_fn(bool bf16, int d, bool causal, bool fixed) {
-  return fixed ? variant_fn_m<true>(bf16, d, causal) : variant_fn_m<false>(bf16, d, causal);
+hipError_t kernel_info(bool bf16, int d, bool causal, bool fixed, int tile, KernelInfo& out) {
+  const void* fn = variant_fn(bf16, d, causal, fixed, tile);
+  hipFuncAttributes attr{};
+  hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, tile_waves(tile) * 64, 0);
+  if (e != hipSuccess) return e;
+  out.rows = block_rows(tile);
+  out.waves = tile_waves(tile);
+  out.vgprs = attr.numRegs;
+  out.lds_bytes = (int)attr.sharedSizeBytes;
+  out.scratch_bytes = (int)attr.localSizeBytes;
+  out.groups_per_cu = per_cu;
+  return hipSuccess;
 }
 
 hipError_t resolve_cfg(bool bf16, int d, bool causal, const AttnParams& prm, LaunchCfg& cfg) {
-  const long long n_qblk = (prm.N + block_rows(d) - 1) / block_rows(d);
-  const long long items = (long long)prm.BH * n_qblk;
   if (cfg.mode == 0) cfg.mode = 1;
+  if (cfg.tile == 0) cfg.tile = 1;
   const bool fixed = cfg.mode == 1;
-  const int variant = (fixed ? 8 : 0) + (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
-  const int slots = resident_groups(variant, variant_fn(bf16, d, causal, fixed));
+  if (!fixed && cfg.tile != 1) return hipErrorInvalidValue;
+  const long long n_qblk = (prm.N + block_rows(cfg.tile) - 1) / block_rows(cfg.tile);
+  const long long items = (long long)prm.BH * n_qblk;
+  const int variant = (cfg.tile == 2 ? 16 : 0) + (fixed ? 8 : 0) + (bf16 ? 4 : 0) + (d == 128 ? 2 : 0) + (causal ? 1 : 0);
+  const int slots = resident_groups(variant, variant_fn(bf16, d, causal, fixed, cfg.tile), tile_waves(cfg.tile) * 64);
   if (slots < 0) return hipErrorInvalidDevice;
   // built-in: heads split over the 8 XCDs when they divide evenly, as many
   // workgroups as run at once, groups of heads that fill one round of items.
@@ -1223,7 +1248,7 @@ hipError_t resolve_cfg(bool bf16, int d, bool causal, const AttnParams& prm, Lau
 
 hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const LaunchCfg& cfg,
                            hipStream_t stream) {
-  const int bm = block_rows(d);
+  const int bm = block_rows(cfg.tile);
   prm.n_qblk = (prm.N + bm - 1) / bm;
   // raw-score margin before the reference maximum moves: 2^2 in probability
   // units for bf16, 2^8 for fp16 (O is divided by the sum of the rounded P,
@@ -1250,7 +1275,8 @@ hipError_t launch_attn_fwd(bool bf16, int d, bool causal, AttnParams prm, const 
   prm.prio = cfg.prio == 1 ? 1 : 0;
   const int grid = prm.n_dom * prm.n_work;
   void* args[] = {&prm};
-  return hipLaunchKernel(variant_fn(bf16, d, causal, fixed), dim3(grid), dim3(kNW * 64), args, 0, stream);
+  return hipLaunchKernel(variant_fn(bf16, d, causal, fixed, cfg.tile), dim3(grid), dim3(tile_waves(cfg.tile) * 64),
+                         args, 0, stream);
 }
 
 }  // namespace ttc

@@ -34,10 +34,17 @@ struct LaunchCfg {
   int grp;      // heads per group in a domain's item order
   int prio;     // 1 on, 2 off
   int mode;     // exponent reference: 1 fixed per item, 2 running maximum
+  int tile;     // 1: 128 query rows per workgroup (4 waves); 2: 256 (8 waves, fixed mode)
 };
 
-// Query rows per workgroup for head dim d.
-int block_rows(int d);
+// Query rows per workgroup of a tile variant (1 or 2).
+int block_rows(int tile);
+
+// Compiled resources of one kernel variant on the current device.
+struct KernelInfo {
+  int rows, waves, vgprs, lds_bytes, scratch_bytes, groups_per_cu;
+};
+hipError_t kernel_info(bool bf16, int d, bool causal, bool fixed, int tile, KernelInfo& out);
 
 // Fill the launch configuration for prm's shape: fields of cfg that are 0
 // get the built-in choice, the others are clamped to what the shape allows.
