@@ -589,6 +589,9 @@ struct Wave {
 // the LDS address, and one wait state separates its write from the load.
 TTC_INLINE void load_one(u32x4 rs, lds_u8* dst, int off, int soff) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+  // the scalar offset must be an SGPR: a compile-time constant would
+  // otherwise be printed as a literal, which the instruction cannot take
+  asm volatile("" : "+s"(soff));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(m), "v"(off), "s"(rs), "s"(soff)
