@@ -80,6 +80,26 @@ def test_shapes(dtype, rows, cols):
     check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"{dtype} {rows}x{cols}")
 
 
+ODD_COLS = {  # byte lengths that are not multiples of 16; the last ones pass 16 KiB (element-wise path)
+    "fp16": [1, 3, 7, 9, 15, 17, 63, 65, 129, 513, 1001, 1023, 2047, 4095, 8191, 8193, 12345],
+    "bf16": [1, 5, 8, 17, 255, 1001, 2049, 8191, 8193],
+    "fp32": [1, 2, 3, 5, 6, 7, 9, 255, 257, 1001, 1022, 2049, 4095, 4097, 4098],
+}
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_odd_widths_every_alignment(dtype):
+    """Rows whose byte length is not a multiple of 16: with 19 rows the row
+    starts run through every element offset within 16 bytes, so the head
+    (before the first 16-byte boundary), the aligned interior and the tail
+    take every split, including rows shorter than 16 bytes that hold no
+    interior at all."""
+    for cols in ODD_COLS[dtype]:
+        x = synth.make_softmax_input(19, cols, dtype, seed=cols + 101)
+        y = run_gpu(x, dtype)
+        check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"odd {dtype} 19x{cols}")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_in_place(dtype):
     x = synth.make_softmax_input(10, 3000, dtype, seed=5)
@@ -88,7 +108,7 @@ def test_in_place(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("cols", [64, 1000, 20000, 70000])
+@pytest.mark.parametrize("cols", [64, 1000, 1001, 9001, 20000, 70000])
 def test_minus_inf_and_nan_rows(dtype, cols):
     """-inf entries weigh 0; an all -inf row and a row holding NaN come out NaN."""
     x = synth.softmax_to_f64(synth.make_softmax_input(6, cols, dtype, seed=cols), dtype).astype(np.float32)
@@ -110,10 +130,10 @@ def test_minus_inf_and_nan_rows(dtype, cols):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("cols", [1554, 2048, 20000, 70000])
+@pytest.mark.parametrize("cols", [1554, 2048, 9001, 20000, 70000])
 def test_large_magnitudes(dtype, cols):
-    """Values of size ~1e4 on every path (element-wise, one wave per row, one
-    workgroup per row, segments):
+    """Values of size ~1e4 on every path (odd byte lengths in registers and
+    element-wise, one wave per row, one workgroup per row, segments):
     the maximum shift keeps every exponent finite, and the rounding of the
     scaled maximum must cancel between numerators and denominator (else the
     relative error reaches ulp(1e4 * log2 e) ~ 1e-3)."""

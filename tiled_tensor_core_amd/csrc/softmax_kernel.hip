@@ -26,8 +26,11 @@
 //     an online pass keeps a running maximum and a sum rescaled when the
 //     maximum moves, then a second pass writes the output;
 //   * rows whose byte length is not a multiple of 16 (odd lengths of 16-bit
-//     data) cannot use 16-byte loads and take an element-wise path with the
-//     register path's three passes, re-reading the row (mostly from cache);
+//     data) start at every alignment: one wave per row loads the aligned
+//     interior with 16-byte loads and the head and tail (each under 16 bytes)
+//     element by element, and keeps the row in registers like the first path;
+//     such rows longer than 16 KiB take an element-wise path that re-reads
+//     the row (mostly from cache);
 //   * within a wave, results combine with xor shuffles;
 //   * 16-byte output stores are non-temporal;
 //   * exponentials are exp2 with log2(e) folded into one multiply-add.
@@ -332,6 +335,86 @@ __global__ void __launch_bounds__(kBlockWaves * 64) softmax_seg(const uint8_t* x
   }
 }
 
+// Rows of at most NCH KiB whose byte length is not a multiple of 16 (odd
+// lengths of 16-bit data, or fp32 rows of a length not divisible by 4), so
+// rows start at every alignment: one wave per row.  The row's 16-byte
+// aligned interior is read with 16-byte buffer loads (64 lanes x 16 bytes per
+// instruction, all issued before the first use), the head before it and the
+// tail after it (each under 16 bytes) element by element by lanes 0-7 and
+// 8-15; everything stays in registers for the three passes (maximum, sum,
+// output), and the interior is written with 16-byte stores.
+template <int T, int NCH>
+__global__ void __launch_bounds__(kWaves * 64) softmax_odd(const uint8_t* x, uint8_t* y, int rows, int cols,
+                                                         float* lse) {
+  using E = Elem<T>;
+  constexpr int EB = E::kBytes;
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * kWaves;
+  const int row_bytes = cols * EB;
+  auto load1 = [&](const uint8_t* p) -> float {
+    if (EB == 4) return *reinterpret_cast<const float*>(p);
+    return E::get(*reinterpret_cast<const uint16_t*>(p), 0);
+  };
+  auto store1 = [&](uint8_t* p, float v) {
+    if (EB == 4)
+      *reinterpret_cast<float*>(p) = v;
+    else
+      *reinterpret_cast<uint16_t*>(p) = (uint16_t)(E::put(v, 0.0f) & 0xffffu);
+  };
+  for (int r = blockIdx.x * kWaves + (threadIdx.x >> 6); r < rows; r += nwaves) {
+    const size_t roff = (size_t)r * (size_t)row_bytes;
+    const int hb = min((int)((16 - (roff & 15)) & 15), row_bytes);   // head bytes, up to the first 16-byte boundary
+    const int ib = ((row_bytes - hb) >> 4) << 4;                      // aligned interior bytes
+    const int tb = row_bytes - hb - ib;                               // tail bytes (< 16)
+    const __amdgpu_buffer_rsrc_t xs = rsrc(x + roff + hb, (uint32_t)ib);
+    u32x4 v[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) v[c] = __builtin_amdgcn_raw_buffer_load_b128(xs, (c * 64 + lane) * 16, 0, 0);
+    // lanes 0-7: head element `lane`; lanes 8-15: tail element `lane - 8`; -inf elsewhere (weight 0)
+    const bool in_head = lane * EB < hb;
+    const bool in_tail = lane >= 8 && (lane - 8) * EB < tb;
+    const size_t eoff = in_head ? roff + (size_t)(lane * EB) : roff + (size_t)(hb + ib + (lane - 8) * EB);
+    const float hv = (in_head || in_tail) ? load1(x + eoff) : -INFINITY;
+    float m = hv;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if ((c * 64 + lane) * 16 >= ib) continue;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int k = 0; k < E::kPerWord; ++k) m = __builtin_elementwise_maximum(m, E::get(v[c][w], k));
+    }
+    m = wave_max(m);
+    const float mc = offset(m);
+    float s = (in_head || in_tail) ? ex2(__builtin_fmaf(hv, kLog2e, -mc)) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if ((c * 64 + lane) * 16 >= ib) continue;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int k = 0; k < E::kPerWord; ++k) s += ex2(__builtin_fmaf(E::get(v[c][w], k), kLog2e, -mc));
+    }
+    s = wave_sum(s);
+    const float inv = 1.0f / s;
+    if (lse && lane == 0) lse[r] = row_lse(mc, s);
+    const __amdgpu_buffer_rsrc_t ys = rsrc(y + roff + hb, (uint32_t)ib);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a = ex2(__builtin_fmaf(E::get(v[c][w], 0), kLog2e, -mc)) * inv;
+        const float b = E::kPerWord == 2 ? ex2(__builtin_fmaf(E::get(v[c][w], 1), kLog2e, -mc)) * inv : 0.0f;
+        o[w] = E::put(a, b);
+      }
+      // pieces past the interior fall outside the buffer and are dropped
+      __builtin_amdgcn_raw_buffer_store_b128(o, ys, (c * 64 + lane) * 16, 0, kStoreNT);
+    }
+    if (in_head || in_tail) store1(y + eoff, ex2(__builtin_fmaf(hv, kLog2e, -mc)) * inv);
+  }
+}
+
 // Any row: element-wise loads (lane j takes elements j, j + 64, ...) and the
 // register path's three passes (maximum, sum, output), the second and third
 // reading the row again.  Used when a row's byte length is not a multiple of
@@ -399,7 +482,20 @@ static hipError_t launch_t(const void* x, void* y, int rows, int cols, float* ls
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* yb = static_cast<uint8_t*>(y);
   if (row_bytes % 16 != 0) {
-    hipLaunchKernelGGL(softmax_elem<T>, dim3(grid_for(rows)), block, 0, stream, xb, yb, rows, cols, lse);
+    const int op = (int)((row_bytes + 1023) / 1024);   // 1 KiB pieces of the interior, at most
+    const dim3 grid(grid_for(rows));
+    if (op <= 1)
+      hipLaunchKernelGGL((softmax_odd<T, 1>), grid, block, 0, stream, xb, yb, rows, cols, lse);
+    else if (op <= 2)
+      hipLaunchKernelGGL((softmax_odd<T, 2>), grid, block, 0, stream, xb, yb, rows, cols, lse);
+    else if (op <= 4)
+      hipLaunchKernelGGL((softmax_odd<T, 4>), grid, block, 0, stream, xb, yb, rows, cols, lse);
+    else if (op <= 8)
+      hipLaunchKernelGGL((softmax_odd<T, 8>), grid, block, 0, stream, xb, yb, rows, cols, lse);
+    else if (op <= kMaxChunks)
+      hipLaunchKernelGGL((softmax_odd<T, kMaxChunks>), grid, block, 0, stream, xb, yb, rows, cols, lse);
+    else
+      hipLaunchKernelGGL(softmax_elem<T>, grid, block, 0, stream, xb, yb, rows, cols, lse);
     return hipGetLastError();
   }
   const int rb = (int)row_bytes;

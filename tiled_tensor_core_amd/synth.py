@@ -183,8 +183,8 @@ SOFTMAX_WORKLOADS = {
     "scores": SoftmaxWorkload("scores", 32768, 2048, "bf16", N03),
     # fp32 rows of 256 KiB: longer than a wave's registers
     "wide": SoftmaxWorkload("wide", 512, 65536, "fp32", N03),
-    # fp16 rows of odd length: no 16-byte alignment of rows
-    "odd": SoftmaxWorkload("odd", 4096, 1001, "fp16", N03),
+    # fp16 rows of odd length: rows start at every 2-byte offset within 16 bytes
+    "odd": SoftmaxWorkload("odd", 32768, 1001, "fp16", N03),
 }
 
 
