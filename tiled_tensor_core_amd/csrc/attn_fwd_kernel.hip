@@ -12,6 +12,8 @@
 //   * an item is 128 query rows of one (batch, head); workgroup = 4 waves,
 //     wave w owns 32 of the item's rows.  Two workgroups share a CU (<= 256
 //     VGPRs per wave, 64 KiB of LDS each), so every SIMD runs two waves.
+//     A second tile (NW = 8) takes 256 rows on 8 waves, one workgroup per
+//     CU: each K/V tile in LDS then serves twice the rows.
 //   * the kernel is persistent: the grid is as many workgroups as the chip
 //     holds at once, each working through a fixed list of items (see the
 //     item order in the kernel).  While an item's last tile is finished,
@@ -51,20 +53,23 @@
 //     4 KiB of LDS so every store writes whole 128-byte row pieces.
 //   * softmax in base 2: p = exp2(s*c - m*c) with c = scale*log2(e) folded
 //     into one FMA; LSE = ln2 * (m*c + log2(l)) at the end.
-//   * the running maximum m used as the exponent reference moves (and O, l
-//     are rescaled by alpha = exp2((m_old - m_new)*c)) only when some row's
-//     tile maximum exceeds it by more than a margin (in log2 units); else
-//     alpha = 1, and the tile skips the 64 multiplies of O.  bf16 uses 2^2
-//     (p <= 4), fp16 2^8 (p <= 256).  With a stale reference a row's
-//     largest P is no longer exactly 1, and its 16-bit rounding would reach
-//     O in full if O were divided by the sum of the unrounded p.  So every
-//     row keeps two sums: l, of the unrounded fp32 p (for LSE), and lo, of
-//     the 16-bit P the matrix cores multiply V by (v_dot2c against a pair of
-//     ones, two P per instruction).  O = acc / lo is then a weighted mean of
-//     the rows of V whose weights sum to 1, whatever the rounding of P:
-//     dominant keys and keys tied at the maximum weigh the same in O's
-//     numerator and denominator.  O / lo and LSE do not depend on the
-//     reference.
+//   * every row keeps two sums: l, of the unrounded fp32 p (for LSE), and
+//     lo, of the 16-bit P the matrix cores multiply V by (v_dot2c against a
+//     pair of ones, two P per instruction).  O = acc / lo is then a weighted
+//     mean of the rows of V whose weights sum to 1, whatever the rounding of
+//     P: dominant keys and keys tied at the maximum weigh the same in O's
+//     numerator and denominator.  Neither O / lo nor LSE depends on the
+//     exponent reference, so the reference need not be the running maximum:
+//   * fixed-reference mode (the default): an item takes its first tile's row
+//     maxima, raised by a headroom, as the reference for all its tiles, so
+//     no later tile reduces a maximum or rescales O.  An item whose P leave
+//     the range this allows is computed again with exact row maxima (rare:
+//     a row must outgrow its first tile by 2^96 for bf16, 2^20 for fp16).
+//   * running-maximum mode (the other variant): the reference m moves (and
+//     O, l, lo are rescaled by alpha = exp2((m_old - m_new)*c)) when some
+//     row's tile maximum exceeds it by more than a margin, 2^2 in
+//     probability units for bf16 and 2^8 for fp16; else alpha = 1 and the
+//     tile skips the 64 multiplies of O.
 //
 // LDS layout: K buffer 0, K buffer 1, V buffer 0, V buffer 1; each a [64][D]
 // tile of bf16/fp16, rows of 2*D bytes split in 16-byte chunks.  The chunk
