@@ -11,17 +11,23 @@
 //
 // gfx950 design:
 //   * a workgroup of 4 waves computes a 256 x 256 tile of C; each wave owns
-//     a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
-//     accumulators (256 fp32 per lane, in the accumulation registers).
-//   * K advances 64 at a time.  A [256 x 64] and W [256 x 64] slices go
-//     from HBM straight into LDS with buffer_load_dwordx4 ... lds (16 bytes
-//     per lane, 1 KiB per wave instruction), double-buffered: the loads of
-//     slice j+1 are issued in the last k16 step of slice j-1 and land while
-//     the MFMAs consume slice j; that last step also reads slice j's first
-//     fragments, so no slice starts by waiting for LDS.
-//     The two buffers are distinct LDS objects and the loop is unrolled by
-//     two, so the compiler can tell the DMA target from the buffer being
-//     read.
+//     a 128 x 128 quarter as 8 x 8 blocks of v_mfma_f32_16x16x32_bf16
+//     accumulators (256 fp32 per lane, in the accumulation registers).  The
+//     16x16x32 form does the same work per cycle as 32x32x16 but draws less
+//     power on random data, so the power-limited chip keeps a higher clock
+//     (measured: +14 % throughput for back-to-back MFMAs on random bf16).
+//   * K advances 64 at a time: A [256 x 64] and W [256 x 64] slices, double-
+//     buffered in LDS.  Each wave moves 16 pieces of 1 KiB per slice
+//     (16 bytes per lane) global -> VGPRs -> LDS: it loads the pieces of
+//     slice j+2 during slice j and writes them to LDS during slice j+1, one
+//     piece after every four MFMAs, so the memory instructions never bunch
+//     up (a wave issuing a run of loads stalls its own MFMAs) and every
+//     load keeps a slice of lead.  Loads straight into LDS
+//     (buffer_load ... lds) measured slower here, bunched or spread.
+//   * a slice is two k32 steps of 64 MFMAs.  Step 0 reads step 1's
+//     fragments; step 1 runs 8 MFMAs, waits for the staged pieces and every
+//     wave, then reads the next slice's fragments between its remaining
+//     MFMAs, so no step starts by waiting for LDS.
 //   * an LDS row holds 64 k values (8 chunks of 16 bytes); the chunk index
 //     is XOR-swizzled with (row >> 1) & 7: the 16 lanes of a phase of a
 //     fragment read (rows r .. r+15 at one chunk, 256 bytes of LDS banks)
@@ -29,19 +35,21 @@
 //   * both operands are K-contiguous (A [M, K], W [N, K]), so both
 //     fragments are plain 16-byte LDS reads.  W is the MFMA's first operand
 //     and A the second: the accumulator block is then C^T, and each lane
-//     holds one row m of C with four runs of 4 consecutive columns n.
+//     holds one row m of C with 4 consecutive columns n per block.
+//   * when K is a multiple of 128 the loads need no per-lane bound check:
+//     a piece's k offset and row step are the scalar offset of its load.
 //   * the bias is the accumulators' starting value, so the matrix cores add
-//     the products to it; the epilogue in registers applies GELU(z) =
-//     z * erfc(-z / sqrt 2) / 2 (erfc from Abramowitz and Stegun 7.1.26)
-//     and rounds to bf16; then each wave stages its 128 x 128 bf16 quarter
-//     in LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled with row & 15,
-//     the 8-byte halves of a chunk swapped in rows with bit 4 set) and
-//     writes C in whole 16-byte pieces, 4 rows of 256 bytes per wave
+//     the products to it; the epilogue in registers applies GELU (erfc from
+//     Abramowitz and Stegun 7.1.26, rearranged so one form serves both
+//     signs) and rounds to bf16; then each wave stages its 128 x 128 bf16
+//     quarter in LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled with
+//     row & 15, the 8-byte halves of a chunk swapped in rows with bit 4 set)
+//     and writes C in whole 16-byte pieces, 4 rows of 256 bytes per wave
 //     instruction.
-//   * tile order: workgroup b runs on XCD b % 8; the tiles are numbered in
-//     groups of 4 tile-rows (column by column within a group), and XCD x
-//     takes a contiguous range of those numbers, so the 32 tiles an XCD
-//     runs at once share 4 row slices of A and 8 of W in its L2.
+//   * tile order: about 256 consecutive workgroups run together, dealt
+//     round-robin to the 8 XCDs; each such window takes a 16 x 16 block of
+//     tiles and each XCD a 4 x 8 part of it, so tiles share operand slices
+//     in the XCD's L2 and across the window in the memory-side cache.
 //   * ragged edges: rows of A or W past M or N read as zero (the buffer
 //     range of the tile's resource); k chunks past K are sent out of range
 //     and read as zero; stores past M or N are dropped.
@@ -71,7 +79,6 @@ constexpr int kWaves = 4;
 constexpr int kRowBytes = kBK * 2;                    // 128 bytes of k per LDS row
 constexpr int kSliceBytes = kBM * kRowBytes;          // 32 KiB per operand slice
 constexpr int kLoadsPerWave = kSliceBytes / (kWaves * 1024);   // 8 per operand
-constexpr int kGroupRows = 4;                         // tile-rows per group in the tile order
 constexpr uint32_t kOut = 0x80000000u;                // a buffer offset past any range
 
 static_assert(kSliceBytes % (kWaves * 1024) == 0, "a slice must split evenly over the waves");
@@ -80,30 +87,34 @@ G_INLINE __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 
-G_INLINE f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+G_INLINE f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 
 G_INLINE u32x4 lds_read16(const lds_u8* p) { return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p); }
 
-// erfc by Abramowitz and Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: erfc(x) ~ t (a1 + a2 t + a3 t^2 + a4 t^3 + a5 t^4) exp(-x^2),
+// GELU(z) = z Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2, with erfc by Abramowitz
+// and Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erfc(x) ~ t (a1 + a2 t + a3 t^2 + a4 t^3 + a5 t^4) exp(-x^2),
 // t = 1 / (1 + p x), for x >= 0 (absolute error below 1.5e-7), and
-// erfc(-x) = 2 - erfc(x).  Over z in [-12, 12] the GELU built on it stays
-// within 4.3e-7 of the exact one in fp32 (at most 1.7e-4 relative where
-// |GELU| > 1e-3), far below the bf16 rounding of the output, at a fifth of
-// the instructions of the library erfcf.
-G_INLINE float erfc_as(float x) {
-  const float ax = __builtin_fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
-  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  const float e = poly * __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return x >= 0.0f ? e : 2.0f - e;
+// erfc(-x) = 2 - erfc(x).  With a = |z| and h = erfc(a / sqrt 2) / 2 both
+// signs reduce to one form: z >= 0 gives z (1 - h), z < 0 gives z h, and
+// both equal max(z, 0) - a h.  The 1/sqrt(2) and the 1/2 are folded into
+// the constants: t = 1 / (1 + (p / sqrt 2) a), exp(-a^2 / 2) =
+// exp2(-a^2 log2(e) / 2), coefficients a_i / 2.  Over z in [-12, 12] it stays
+// within 4.3e-7 of the exact GELU in fp32 (at most 1.7e-4 relative where
+// |GELU| > 1e-3), far below the bf16 rounding of the output.
+G_INLINE float gelu(float z) {
+  const float a = __builtin_fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.23164190f, a, 1.0f));   // p / sqrt 2, p = 0.3275911
+  const float e = __builtin_amdgcn_exp2f((a * -0.72134752044448170f) * a);        // -log2(e) / 2
+  float q = __builtin_fmaf(t, 0.5307027145f, -0.7265760135f);                   // a5/2, a4/2
+  q = __builtin_fmaf(t, q, 0.7107068705f);                                     // a3/2
+  q = __builtin_fmaf(t, q, -0.142248368f);                                     // a2/2
+  q = __builtin_fmaf(t, q, 0.127414796f);                                      // a1/2
+  return __builtin_fmaf(-(a * e), q * t, __builtin_fmaxf(z, 0.0f));
 }
-// GELU(z) = z * Phi(z), Phi(z) = erfc(-z / sqrt(2)) / 2 (no cancellation for
-// negative z).
-G_INLINE float gelu(float z) { return 0.5f * z * erfc_as(-0.70710678118654752f * z); }
 
 // The accumulator already holds the bias (when there is one); only the
 // activation is left.
@@ -116,7 +127,10 @@ G_INLINE float activation(float z) {
   }
 }
 
-template <int EPI>
+// KFULL: K is a multiple of 2 * kBK, so every slice the loop computes lies
+// inside K and the loads need no per-lane bound check (the k offset of a
+// slice and the row step of a piece are the scalar offset of the load).
+template <int EPI, bool KFULL>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[kSliceBytes];
@@ -133,14 +147,31 @@ gemm_kernel(GemmParams p) {
   const int wm = wave >> 1, wn = wave & 1;             // this wave's quarter of the tile
 
   // ---- tile of this workgroup ---------------------------------------------
+  // Workgroups start in index order, dealt round-robin to the 8 XCDs (b % 8),
+  // 32 at a time per XCD (one per CU), so about 256 consecutive indices run
+  // together.  Each such window takes a 16 x 16 block of tiles, and XCD x
+  // a 4 x 8 part of it: the 32 tiles on one XCD share 4 row slices of A and 8
+  // of W in its L2, and the 256 tiles of a window share 16 + 16 in the
+  // memory-side cache.  Windows run along a band of 16 tile-rows, so the next
+  // window keeps the band's A.  Partial windows and partial blocks at the
+  // edges take their tiles in plain order.
   const int nt = (int)gridDim.x, b = (int)blockIdx.x;
-  const int x = b & 7, i = b >> 3, q = nt >> 3, r = nt & 7;
-  const int t = x * q + min(x, r) + i;                 // XCD x: tiles [x*q + min(x, r), +q + (x < r))
-  const int span = kGroupRows * p.tiles_n;
-  const int first_m = (t / span) * kGroupRows;
-  const int gm = min(kGroupRows, p.tiles_m - first_m);
-  const int u = t - (t / span) * span;
-  const int tm = first_m + u % gm, tn = u / gm;
+  const int full = nt & ~255;
+  const int t = b < full ? (b & ~255) + 32 * (b & 7) + ((b >> 3) & 31) : b;
+  const int band = 16 * p.tiles_n;                     // tiles in a band of 16 tile-rows
+  const int br = t / band, hm = min(16, p.tiles_m - 16 * br);
+  const int ub = t - br * band;                        // index inside the band
+  const int bc = ub / (16 * hm), hn = min(16, p.tiles_n - 16 * bc);
+  const int v = ub - bc * 16 * hm;                     // index inside the hm x hn block
+  int tm, tn;
+  if (hm == 16 && hn == 16) {
+    const int part = v >> 5, w = v & 31;               // 4 x 8 part of the block, tile in it (column-major)
+    tm = 16 * br + 4 * (part >> 1) + (w & 3);
+    tn = 16 * bc + 8 * (part & 1) + (w >> 2);
+  } else {
+    tm = 16 * br + v % hm;
+    tn = 16 * bc + v / hm;
+  }
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int M = p.M, N = p.N, K = p.K;
 
@@ -151,126 +182,121 @@ gemm_kernel(GemmParams p) {
   const uint32_t a_rows = (uint32_t)min(kBM, M - m0), w_rows = (uint32_t)min(kBN, N - n0);
   const __amdgpu_buffer_rsrc_t ars = rsrc(p.a + (size_t)m0 * K, a_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wrs = rsrc(p.w + (size_t)n0 * K, w_rows * (uint32_t)K * 2u);
-  int ld_row[kLoadsPerWave], ld_k[kLoadsPerWave];
+  // Piece s of a wave covers rows row0 + 8 s: the swizzle term (row >> 1) & 7
+  // then differs between even and odd s only (by 4), so two k offsets serve
+  // all pieces, and the row step is a scalar offset.
+  const int row0 = wave * kLoadsPerWave * 8 + (lane >> 3);
+  int ld_k[2];
 #pragma unroll
-  for (int s = 0; s < kLoadsPerWave; ++s) {
-    const int idx = (wave * kLoadsPerWave + s) * 64 + lane;
-    const int row = idx >> 3;
-    ld_row[s] = row;
-    ld_k[s] = 8 * ((idx & 7) ^ ((row >> 1) & 7));
-  }
-  auto load_slice = [&](lds_u8* abuf, lds_u8* wbuf, int k0) {
+  for (int par = 0; par < 2; ++par) ld_k[par] = 8 * ((lane & 7) ^ (((row0 >> 1) + 4 * par) & 7));
+  uint32_t ld_off[2];
 #pragma unroll
-    for (int s = 0; s < kLoadsPerWave; ++s) {
-      const int k = k0 + ld_k[s];
-      const uint32_t off = k < K ? (uint32_t)(ld_row[s] * K + k) * 2u : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(abuf + (wave * kLoadsPerWave + s) * 1024), 16, off,
-                                               0, 0, 0);
+  for (int par = 0; par < 2; ++par) ld_off[par] = (uint32_t)(row0 * K + ld_k[par]) * 2u;
+  // A slice moves global -> VGPRs -> LDS: each wave loads its 16 pieces of
+  // slice j+2 into registers during slice j and writes them to LDS during
+  // slice j+1, so the loads spread over the slice and still have a slice of
+  // lead.
+  u32x4 ra[kLoadsPerWave], rw[kLoadsPerWave];
+  auto gload = [&](__amdgpu_buffer_rsrc_t rs, int s, int k0) -> u32x4 {
+    if constexpr (KFULL) {
+      // loads of the slices past K (issued by the last two slices, never
+      // used) read the next rows, or nothing past the last row
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, ld_off[s & 1], (uint32_t)(k0 + 8 * s * K) * 2u, 0);
+    } else {
+      const int k = k0 + ld_k[s & 1];
+      const uint32_t off = k < K ? (uint32_t)((row0 + 8 * s) * K + k) * 2u : kOut;
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < kLoadsPerWave; ++s) {
-      const int k = k0 + ld_k[s];
-      const uint32_t off = k < K ? (uint32_t)(ld_row[s] * K + k) * 2u : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void*)(wbuf + (wave * kLoadsPerWave + s) * 1024), 16, off,
-                                               0, 0, 0);
+  };
+  auto swrite = [&](lds_u8* buf, int s, u32x4 v) {
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(buf + (wave * kLoadsPerWave + s) * 1024 + lane * 16) = v;
+  };
+  // piece q of 16 (0-7 A, 8-15 W): write the staged value into the next
+  // slice's buffer, then load the same piece of the slice after it
+  auto stage_piece = [&](lds_u8* nabuf, lds_u8* nwbuf, int q, int k2) {
+    if (q < kLoadsPerWave) {
+      swrite(nabuf, q, ra[q]);
+      ra[q] = gload(ars, q, k2);
+    } else {
+      swrite(nwbuf, q - kLoadsPerWave, rw[q - kLoadsPerWave]);
+      rw[q - kLoadsPerWave] = gload(wrs, q - kLoadsPerWave, k2);
     }
   };
 
-  // ---- fragment reads: lane l reads row l % 32 of a 32-row block, k chunk
-  // 2*kk + l / 32 of the slice, at its swizzled place.
-  int rd[4];
+  // ---- fragment reads: lane l reads row l % 16 of a 16-row block, k chunk
+  // 4*ks + l / 16 of the slice (k32 step ks), at its swizzled place.
+  int rd[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) rd[kk] = (lane & 31) * kRowBytes + (((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4);
+  for (int ks = 0; ks < 2; ++ks) rd[ks] = (lane & 15) * kRowBytes + (((4 * ks + (lane >> 4)) ^ ((lane >> 1) & 7)) << 4);
   const int a_base = wm * 128 * kRowBytes, w_base = wn * 128 * kRowBytes;
 
-  // Accumulators start at the bias (register 4g + jj of a lane in column
-  // block nb is column nb*32 + 8g + 4*(lane / 32) + jj, for every row block),
-  // so the matrix cores add the products on top and no epilogue add is left.
-  f32x16 acc[4][4];
+  // Accumulators start at the bias (register r of a lane in column block nb
+  // is column nb*16 + 4*(lane / 16) + r, for every row block), so the matrix
+  // cores add the products on top and no epilogue add is left.
+  f32x4 acc[8][8];
   {
-    const int h4 = 4 * (lane >> 5);
+    const int h4 = 4 * (lane >> 4);
     const __amdgpu_buffer_rsrc_t brs = rsrc(p.bias, EPI != 0 ? (uint32_t)N * 4u : 0u);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      f32x16 bv = {};
+    for (int nb = 0; nb < 8; ++nb) {
+      f32x4 bv = {};
+      asm volatile("" : "+v"(bv));   // distinct starting values: each block accumulates in place
       if constexpr (EPI != 0) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + nb * 32 + 8 * g + h4;
-          const f32x4 b4 = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, n < N ? (uint32_t)n * 4u : kOut, 0, 0));
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) bv[4 * g + jj] = b4[jj];
-        }
+        const int n = n0 + wn * 128 + nb * 16 + h4;
+        bv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, n < N ? (uint32_t)n * 4u : kOut, 0, 0));
       }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = bv;
+      for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = bv;
     }
   }
 
-  // Fragment reads run one k16 step ahead of the MFMAs that use them, and
-  // scheduling group barriers interleave them with the MFMAs, one read
-  // between every two MFMAs.  LDS is the busiest unit here -- the loads
-  // write 64 KiB and the fragment reads read 128 KiB per slice per compute
-  // unit -- and a burst of reads from all four waves queued behind the load
-  // traffic stalled the matrix cores; spread out, the same work ran 3-8 %
-  // faster.  A scheduling barrier closes each step, so no read moves up
-  // into an earlier step.
-  auto read_frags = [&](const lds_u8* abuf, const lds_u8* wbuf, int kk, u32x4 (&af)[4], u32x4 (&wf)[4]) {
+  auto read_frags = [&](const lds_u8* abuf, const lds_u8* wbuf, int ks, u32x4 (&af)[8], u32x4 (&wf)[8]) {
+    af[0] = lds_read16(abuf + a_base + rd[ks]);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read16(abuf + a_base + mb * 32 * kRowBytes + rd[kk]);
+    for (int nb = 0; nb < 8; ++nb) wf[nb] = lds_read16(wbuf + w_base + nb * 16 * kRowBytes + rd[ks]);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) wf[nb] = lds_read16(wbuf + w_base + nb * 32 * kRowBytes + rd[kk]);
+    for (int mb = 1; mb < 8; ++mb) af[mb] = lds_read16(abuf + a_base + mb * 16 * kRowBytes + rd[ks]);
   };
-  // The first k16 step of a slice reads its fragments during the last step
-  // of the slice before: that step waits for the next slice's loads and
-  // holds the barrier after its first four MFMAs, then reads the next
-  // slice's first fragments and issues the loads of the slice after it
-  // (into the buffer just read) between its remaining MFMAs.  So no slice
-  // starts by waiting for LDS.  Two fragment register sets alternate:
-  // A (af0/wf0) for steps 0 and 2, B for steps 1 and 3.
-  u32x4 af0[4], wf0[4];
-  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, const lds_u8* nabuf, const lds_u8* nwbuf,
-                     lds_u8* dabuf, lds_u8* dwbuf, int dk0) {
-    u32x4 af1[4], wf1[4];
+  // A slice is two k32 steps of 64 MFMAs.  Step 0 reads step 1's fragments
+  // and stages the next slice's 16 pieces; step 1 runs 8 MFMAs, waits for
+  // the pieces and every wave, then reads the next slice's step-0 fragments
+  // between its remaining 56 MFMAs.
+  u32x4 af0[8], wf0[8];
+  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, lds_u8* nabuf, lds_u8* nwbuf, int k2) {
+    u32x4 af1[8], wf1[8];
+    read_frags(abuf, wbuf, 1, af1, wf1);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      if (kk & 1)
-        read_frags(abuf, wbuf, kk + 1, af0, wf0);
-      else
-        read_frags(abuf, wbuf, kk + 1, af1, wf1);
+    for (int q = 0; q < 16; ++q) stage_piece(nabuf, nwbuf, q, k2);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = (kk & 1) ? mfma(wf1[nb], af1[mb], acc[mb][nb]) : mfma(wf0[nb], af0[mb], acc[mb][nb]);
+      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma(wf0[nb], af0[mb], acc[mb][nb]);
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    // step 3
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[0][nb] = mfma(wf1[nb], af1[0], acc[0][nb]);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[0][nb] = mfma(wf1[nb], af1[0], acc[0][nb]);
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(nabuf, nwbuf, 0, af0, wf0);
-    load_slice(dabuf, dwbuf, dk0);
 #pragma unroll
-    for (int mb = 1; mb < 4; ++mb)
+    for (int mb = 1; mb < 8; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(wf1[nb], af1[mb], acc[mb][nb]);
+      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma(wf1[nb], af1[mb], acc[mb][nb]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < 16; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -280,15 +306,27 @@ gemm_kernel(GemmParams p) {
   // The last two slices issue loads past K, which only write zeros into
   // LDS; the barrier after the loop waits for them.
   const int nk = ((K + kBK - 1) / kBK + 1) & ~1;
-  load_slice(A0, W0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s2 = 0; s2 < kLoadsPerWave; ++s2) {
+    ra[s2] = gload(ars, s2, 0);
+    rw[s2] = gload(wrs, s2, 0);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < kLoadsPerWave; ++s2) {
+    swrite(A0, s2, ra[s2]);
+    swrite(W0, s2, rw[s2]);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < kLoadsPerWave; ++s2) ra[s2] = gload(ars, s2, kBK);
+#pragma unroll
+  for (int s2 = 0; s2 < kLoadsPerWave; ++s2) rw[s2] = gload(wrs, s2, kBK);
   __syncthreads();
-  load_slice(A1, W1, kBK);
   read_frags(A0, W0, 0, af0, wf0);
   for (int j = 0; j < nk; j += 2) {
-    compute(A0, W0, A1, W1, A0, W0, (j + 2) * kBK);   // slice j; reads slice j+1, loads slice j+2
-    compute(A1, W1, A0, W0, A1, W1, (j + 3) * kBK);   // slice j+1; reads slice j+2, loads slice j+3
+    compute(A0, W0, A1, W1, (j + 2) * kBK);   // slice j; writes slice j+1, loads slice j+2
+    compute(A1, W1, A0, W0, (j + 3) * kBK);   // slice j+1; writes slice j+2, loads slice j+3
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // every wave is done reading the slices: LDS is free for the output.  The
   // scheduling barriers keep the accumulator reads of the epilogue below
   // it (hoisted above, all 256 values would sit in VGPRs at once).
@@ -297,39 +335,42 @@ gemm_kernel(GemmParams p) {
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- epilogue -------------------------------------------------------------
-  // Lane l holds, for block (mb, nb), row m = mb*32 + l % 32 of the wave's
-  // quarter and columns nb*32 + 8g + 4*(l / 32) + jj for register 4g + jj.
-  // Each wave stages its quarter in one 32 KiB LDS object.
+  // Lane l holds, for block (mb, nb), row m = mb*16 + l % 16 of the wave's
+  // quarter and columns nb*16 + 4*(l / 16) + r for register r.  Each wave
+  // stages its quarter in one 32 KiB LDS object.
   lds_u8* const stage = wave == 0 ? A0 : wave == 1 ? W0 : wave == 2 ? A1 : W1;
-  const int h = lane >> 5, ml = lane & 31;
+  // the lane index again, from the execution mask (all lanes are active),
+  // so no register holds it through the loop and the epilogue's addresses
+  // are computed here
+  int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(el));
+  const int g4 = el >> 4, ml = el & 15;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int row = mb * 32 + ml;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float v0 = activation<EPI>(acc[mb][nb][4 * g + 0]);
-        const float v1 = activation<EPI>(acc[mb][nb][4 * g + 1]);
-        const float v2 = activation<EPI>(acc[mb][nb][4 * g + 2]);
-        const float v3 = activation<EPI>(acc[mb][nb][4 * g + 3]);
-        u32x2 pk;
-        pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v0, v1}, bf16x2));
-        pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v2, v3}, bf16x2));
-        const int chunk = nb * 4 + g;                  // 16-byte chunk of the 256-byte row
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * (h ^ ((row >> 4) & 1))) = pk;
-      }
-      __builtin_amdgcn_sched_barrier(0);   // one block at a time: no hoisting of every block's values
+    for (int mb = 0; mb < 8; ++mb) {
+      const int row = mb * 16 + ml;
+      const float v0 = activation<EPI>(acc[mb][nb][0]);
+      const float v1 = activation<EPI>(acc[mb][nb][1]);
+      const float v2 = activation<EPI>(acc[mb][nb][2]);
+      const float v3 = activation<EPI>(acc[mb][nb][3]);
+      u32x2 pk;
+      pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v0, v1}, bf16x2));
+      pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v2, v3}, bf16x2));
+      const int chunk = nb * 2 + (g4 >> 1);            // 16-byte chunk of the 256-byte row
+      const int h = g4 & 1;                            // 8-byte half of the chunk
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * (h ^ ((row >> 4) & 1))) = pk;
+      if (mb & 1) __builtin_amdgcn_sched_barrier(0);   // two blocks at a time: no hoisting of every block's values
     }
   }
   // each wave reads back only what it wrote
   const uint32_t c_rows = (uint32_t)min(kBM, M - m0);
   const __amdgpu_buffer_rsrc_t crs = rsrc(p.c + (size_t)m0 * N, c_rows * (uint32_t)N * 2u);
-  const int c = lane & 15;
+  const int c = el & 15;
   const int n = n0 + wn * 128 + c * 8;
 #pragma unroll
   for (int it = 0; it < 32; ++it) {
-    const int row = it * 4 + (lane >> 4);
+    const int row = it * 4 + (el >> 4);
     u32x4 v = lds_read16(stage + row * 256 + ((c ^ (row & 15)) << 4));
     if ((it >> 2) & 1) v = (u32x4){v[2], v[3], v[0], v[1]};   // rows with bit 4 set hold their halves swapped
     const uint32_t off = n < N ? ((uint32_t)(wm * 128 + row) * (uint32_t)N + (uint32_t)n) * 2u : kOut;
@@ -344,10 +385,20 @@ hipError_t launch_gemm(int epi, const GemmParams& prm, hipStream_t stream) {
   const long long tiles = (long long)p.tiles_m * p.tiles_n;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)tiles), block(kWaves * 64);
+  const bool kfull = p.K % (2 * kBK) == 0;
   switch (epi) {
-    case 0: hipLaunchKernelGGL(gemm_kernel<0>, grid, block, 0, stream, p); break;
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, 0, stream, p); break;
+    case 0:
+      if (kfull) hipLaunchKernelGGL((gemm_kernel<0, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((gemm_kernel<0, false>), grid, block, 0, stream, p);
+      break;
+    case 1:
+      if (kfull) hipLaunchKernelGGL((gemm_kernel<1, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((gemm_kernel<1, false>), grid, block, 0, stream, p);
+      break;
+    default:
+      if (kfull) hipLaunchKernelGGL((gemm_kernel<2, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((gemm_kernel<2, false>), grid, block, 0, stream, p);
+      break;
   }
   return hipGetLastError();
 }
