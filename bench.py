@@ -151,6 +151,18 @@ def time_workload(attn, torch, w, causal, steps, warmup, inputs, warmup_s=WARMUP
     return r
 
 
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, causal, bits, budget_s):
     """The fp64 oracle on whole heads of the workload until ``budget_s`` of
     CPU time has passed; FLOPs credited with the same algorithmic count."""
@@ -180,10 +192,14 @@ def cpu_baseline(w, causal, bits, budget_s):
             if elapsed >= budget_s:
                 break
     f = flops(1, heads, w.N, w.d, causal)
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                   if p.get("user_api") == "blas"})
     return {
         "value": f / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": host_cpu_model(),
+        "blas": ", ".join(blas) or None,
         "kind": "oracle",
         "sample": f"{heads} of {w.B * w.H} heads (all {w.N} rows each), fp64 numpy, "
                   f"{elapsed:.1f} s; wall {time.perf_counter() - t0:.1f} s",
@@ -474,6 +490,81 @@ def run_unfused(a, torch, attn, synth):
     print(json.dumps(out), flush=True)
 
 
+# Shapes of equal non-causal work (B*H*N^2 fixed, d = 128, bf16) whose items
+# of 128 query rows hold 16, 32 and 64 key tiles of 64: the time split fit.
+SPLIT_SHAPES = [(8, 128, 1024), (8, 32, 2048), (8, 8, 4096)]
+
+
+def run_split(a, torch, attn, synth):
+    """Where the attention kernel's time goes, from launch timings alone.
+
+    Non-causal, a launch does items * tiles tile steps (tiles = N / 64 per
+    128-row item) plus a fixed cost per item (loading Q, the first scores,
+    the last P V, the epilogue).  The three shapes have the same number of
+    tile steps and 2048, 4096 and 8192 items, so a straight-line fit of the
+    kernel time against the item count gives the cost of the tile steps (the
+    intercept) and of one item (the slope).  A causal item of query block qb
+    does 2 (qb + 1) tile steps, the last two of them masked; the causal time
+    minus the fit's prediction for those steps and items is the extra cost of
+    the masked diagonal steps."""
+    d = 128
+    rows = []
+    for B, H, N in SPLIT_SHAPES:
+        w = synth.Workload(f"split{N}", B, H, N, d, "bf16", (False, True), synth.N01, synth.N01, synth.N01)
+        print(f"[bench] split: generating {w.describe()}", file=sys.stderr, flush=True)
+        inputs = tuple(synth.to_torch(x, w.dtype, "cuda") for x in synth.make_workload(w))
+        nq = (N + 127) // 128
+        for causal in (False, True):
+            r = time_workload(attn, torch, w, causal, a.steps, a.warmup, inputs, a.warmup_seconds)
+            steps = B * H * (nq * (nq + 1) if causal else nq * (N // 64))
+            rows.append({"B": B, "H": H, "N": N, "causal": causal, "items": B * H * nq, "tile_steps": steps,
+                         "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                         "tflops": round(r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12, 2)})
+            print(f"[bench] split: timed N={N} causal={causal}", file=sys.stderr, flush=True)
+        del inputs
+        torch.cuda.empty_cache()
+    nc = [r for r in rows if not r["causal"]]
+    x = [r["items"] for r in nc]
+    y = [r["kernel_ms_mean"] for r in nc]
+    n = len(x)
+    mx, my = sum(x) / n, sum(y) / n
+    slope = sum((xi - mx) * (yi - my) for xi, yi in zip(x, y)) / sum((xi - mx) ** 2 for xi in x)
+    icpt = my - slope * mx
+    t_step = icpt / nc[0]["tile_steps"]          # ms per tile step, device-wide
+    split = {}
+    for r in rows:
+        if not r["causal"]:
+            continue
+        steps_ms = r["tile_steps"] * t_step
+        item_ms = r["items"] * slope
+        diag_ms = r["kernel_ms_mean"] - steps_ms - item_ms
+        split[f"causal N={r['N']}"] = {
+            "kernel_ms_mean": r["kernel_ms_mean"],
+            "tile_steps_share": round(steps_ms / r["kernel_ms_mean"], 4),
+            "per_item_share": round(item_ms / r["kernel_ms_mean"], 4),
+            "masked_diagonal_extra_share": round(diag_ms / r["kernel_ms_mean"], 4),
+        }
+    for r in nc:
+        split[f"non-causal N={r['N']}"] = {
+            "kernel_ms_mean": r["kernel_ms_mean"],
+            "tile_steps_share": round(r["tile_steps"] * t_step / r["kernel_ms_mean"], 4),
+            "per_item_share": round(r["items"] * slope / r["kernel_ms_mean"], 4),
+        }
+    out = {
+        "metric": "attention fwd time split (launch timings, straight-line fit over equal-work shapes)",
+        "unit": "share of the kernel time",
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"shapes": [f"B={B},H={H},N={N},d={d}" for B, H, N in SPLIT_SHAPES]},
+        "fit": {"ms_per_tile_step_device": t_step, "ms_per_item_device": slope,
+                "item_cost_in_tile_steps": round(slope / t_step, 3),
+                "tile_step_tflops": round(2 * 2 * 128 * 64 * d / (t_step * 1e-3) / 1e12, 1)},
+        "runs": rows,
+        "split": split,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,6 +584,9 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=WARMUP_MIN_S,
                     help="minimum warm-up time in seconds (0: exactly --warmup steps, as counter runs want)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--split", action="store_true",
+                    help="time equal-work attention shapes and split the kernel time into tile steps, "
+                         "per-item costs and the masked diagonal steps")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (causal and non-causal) and report them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -533,6 +627,9 @@ def main():
         return
     if a.kernel == "unfused":
         run_unfused(a, torch, attn, synth)
+        return
+    if a.split:
+        run_split(a, torch, attn, synth)
         return
     w = synth.WORKLOADS[a.workload]
     causal = w.causal[-1]

@@ -51,8 +51,10 @@ def _check(c, a64, w64, bias, epi, tag, rows=None):
     assert np.all(err <= bound), f"{tag}: worst err/bound {worst}"
 
 
-SHAPES = [  # M, N, K: one partial tile; exact tiles; ragged in all three with a K tail; tiny
+SHAPES = [  # M, N, K: one partial tile; exact tiles; ragged in all three with a K tail; tiny;
+    # K a multiple of 128 (loads without bound checks) with ragged M and N
     (300, 264, 200), (256, 256, 64), (512, 512, 128), (1000, 776, 328), (1, 8, 8), (17, 24, 72), (257, 8, 4104),
+    (1000, 776, 256), (300, 264, 384), (33, 40, 128),
 ]
 
 
@@ -63,6 +65,17 @@ def test_parity(M, N, K, epi):
     c = _run(a, w, b, epi)
     _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), epi,
            f"{M}x{N}x{K} epi={epi}")
+
+
+def test_many_tiles_every_element():
+    """342 tiles of 256 x 256 (one full window of 256 concurrently running
+    tiles and a partial one, ragged in M and N): every element against the
+    oracle, so a tile computed twice or never would show."""
+    M, N, K = 17 * 256 + 5, 19 * 256 - 3, 128
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=21)
+    c = _run(a, w, b, EPI_BIAS_GELU)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
+           f"{M}x{N}x{K} every element")
 
 
 def test_gelu_range_and_large_values():
