@@ -71,7 +71,7 @@ def test_many_tiles_every_element():
     """342 tiles of 256 x 256 (one full window of 256 concurrently running
     tiles and a partial one, ragged in M and N): every element against the
     oracle, so a tile computed twice or never would show."""
-    M, N, K = 17 * 256 + 5, 19 * 256 - 3, 128
+    M, N, K = 17 * 256 + 5, 19 * 256 - 8, 128   # N a multiple of 8
     a, w, b = synth.make_gemm_inputs(M, N, K, seed=21)
     c = _run(a, w, b, EPI_BIAS_GELU)
     _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
