@@ -32,8 +32,11 @@
  * library allocates nothing and keeps no pointer after it returns.  The call
  * only enqueues work on `stream`.
  *
- * Alignment: x and y must be 16-byte aligned.  Rows whose byte length is a
- * multiple of 16 take the vector path; other rows are correct but slower.
+ * Alignment: x and y must be 16-byte aligned.  Rows of any length are read
+ * with 16-byte loads where they are 16-byte aligned (rows whose byte length
+ * is not a multiple of 16 start at every alignment: their head and tail,
+ * under 16 bytes each, are read element by element); rows of odd byte
+ * length longer than 16 KiB take a slower element-wise path.
  *
  * Errors: arguments are checked on the host before any HIP call and return
  * the attn_status codes of attn.h (ATTN_ERR_NULL, ATTN_ERR_SHAPE,
