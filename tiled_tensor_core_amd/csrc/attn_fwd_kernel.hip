@@ -596,6 +596,9 @@ TTC_INLINE void load_one(u32x4 rs, lds_u8* dst, int off, int soff) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
   // the scalar offset must be an SGPR: a compile-time constant would
   // otherwise be printed as a literal, which the instruction cannot take
+  // (soff is uniform by construction; readfirstlane states it where the
+  // compiler cannot prove it)
+  soff = __builtin_amdgcn_readfirstlane(soff);
   asm volatile("" : "+s"(soff));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -964,17 +967,22 @@ attn_fwd_kernel(AttnParams p) {
     // Pipelined step j loads K_{j+2} (if any) into the K buffer tile j used and
     // V_{j+1} into the other V buffer, both wholly inside the sequence, one
     // 1 KiB piece at a time.  Even j: K_{j+1} is in K1, V_j in V0.
+    // When step j has no K_{j+2} (the last step of an item whose tiles all
+    // run here), its K loads still issue, sent out of range through the lane
+    // offset (the part of the address the buffer's range check covers): no
+    // memory is read, and the step needs no branch per load.
     int j = 0;
+    int koob = 0;   // 0, or an offset past the head for the K loads of this step
     auto ld_even = [&](int k) {
       if (k < PER_W) {
-        if (j + 2 < n_tiles) load_one(krs, K0 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
+        load_one(krs, K0 + wofs + k * 1024, koff_t(k) | koob, (j + 2) * TILE_BYTES + k * 1024);
       } else {
         load_one(vrs, V1 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
     };
     auto ld_odd = [&](int k) {
       if (k < PER_W) {
-        if (j + 2 < n_tiles) load_one(krs, K1 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
+        load_one(krs, K1 + wofs + k * 1024, koff_t(k) | koob, (j + 2) * TILE_BYTES + k * 1024);
       } else {
         load_one(vrs, V0 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
@@ -983,6 +991,7 @@ attn_fwd_kernel(AttnParams p) {
     for (; j + 1 < n_pipe; j += 2) {
       wait_all();
       progress();
+      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)   // no maximum, no rescale
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
       else if (w.moved)
@@ -992,6 +1001,7 @@ attn_fwd_kernel(AttnParams p) {
       ++j;
       wait_all();
       progress();
+      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sb, sa, K0, V1, ld_odd);
       else if (w.moved)
@@ -1003,6 +1013,7 @@ attn_fwd_kernel(AttnParams p) {
     if (j < n_pipe) {
       wait_all();
       progress();
+      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
       else if (w.moved)
@@ -1021,9 +1032,10 @@ attn_fwd_kernel(AttnParams p) {
     auto ld_any = [&](int k) {
       const bool odd = j & 1;
       if (k < PER_W) {
-        if (j + 2 < n_tiles)
-          load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, koff_t(k) + (j + 2 == j_tail ? tail_delta(k) : 0),
-                   (j + 2) * TILE_BYTES + k * 1024);
+        // no K_{j+2}: the loads go out of range, as in the pipelined steps
+        const int oob = j + 2 < n_tiles ? 0 : (int)0x80000000;
+        load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, (koff_t(k) + (j + 2 == j_tail ? tail_delta(k) : 0)) | oob,
+                 (j + 2) * TILE_BYTES + k * 1024);
       } else {
         const int t = k - PER_W;
         load_one(vrs, (odd ? V0 : V1) + wofs + t * 1024, voff + (j + 1 == j_tail ? tail_delta(t) : 0),

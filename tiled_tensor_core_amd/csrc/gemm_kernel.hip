@@ -199,9 +199,12 @@ gemm_kernel(GemmParams p) {
   u32x4 ra[kLoadsPerWave], rw[kLoadsPerWave];
   auto gload = [&](__amdgpu_buffer_rsrc_t rs, int s, int k0) -> u32x4 {
     if constexpr (KFULL) {
-      // loads of the slices past K (issued by the last two slices, never
-      // used) read the next rows, or nothing past the last row
-      return __builtin_amdgcn_raw_buffer_load_b128(rs, ld_off[s & 1], (uint32_t)(k0 + 8 * s * K) * 2u, 0);
+      // the loads of the two slices past K (issued by the last two slices,
+      // never used) are sent out of range through the lane offset, which is
+      // what the buffer's range check covers, so nothing is read
+      const bool in = k0 < K;
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, in ? ld_off[s & 1] : kOut, in ? (uint32_t)(k0 + 8 * s * K) * 2u : 0u,
+                                                   0);
     } else {
       const int k = k0 + ld_k[s & 1];
       const uint32_t off = k < K ? (uint32_t)((row0 + 8 * s) * K + k) * 2u : kOut;
