@@ -240,6 +240,8 @@ struct Wave {
   // mode keeps only k-step 0 and forms kk's as kro[0] ^ 32 kk (the swizzle
   // index and the chunk 2 kk of the operand share no bits)
   int kro[FIXED ? 1 : DK];
+  mutable int kcur;  // fixed mode: the offset of the k-step being read (both key blocks use it)
+  mutable int kbase; // fixed mode: an opaque copy of kro[0], taken once per tile
   int vro[DT];       // byte offset of this lane's V^T operand in a V tile, per d-block
 
   TTC_INLINE static float at(const f32x16 (&s)[KB], int v) { return s[v >> 4][v & 15]; }
@@ -249,10 +251,15 @@ struct Wave {
   TTC_INLINE u32x4 kop(int i, const lds_u8* kt) const {
     int kr;
     if constexpr (FIXED) {
-      // an opaque copy per read: the compiler must not keep all DK offsets live
-      int k0 = kro[0];
-      asm volatile("" : "+v"(k0));
-      kr = (i / KB) == 0 ? k0 : (k0 ^ (32 * (i / KB)));
+      // an opaque copy per k-step (the reads of a tile come in order, both
+      // key blocks of a k-step together): the compiler must not keep all DK
+      // offsets live
+      if (i == 0) {
+        kbase = kro[0];
+        asm volatile("" : "+v"(kbase));
+      }
+      if (i % KB == 0) kcur = (i / KB) == 0 ? kbase : (kbase ^ (32 * (i / KB)));
+      kr = kcur;
     } else {
       kr = kro[i / KB];
     }
@@ -734,10 +741,13 @@ attn_fwd_kernel(AttnParams p) {
   lane_offsets(lane, koff, voff);
   // lane offset of K load t (an opaque copy, so the compiler does not keep
   // all PER_W of them live across the loop)
+  int kload = 0;   // an opaque copy of koff, taken once per step (at piece 0)
   auto koff_t = [&](int t) {
-    int k = koff;
-    asm volatile("" : "+v"(k));
-    return t == 0 ? k : (k ^ (64 * t));
+    if (t == 0) {
+      kload = koff;
+      asm volatile("" : "+v"(kload));
+    }
+    return t == 0 ? kload : (kload ^ (64 * t));
   };
   // The last tile's rows past N (if any) repeat row N-1 (finite values whose
   // scores are masked, so they add exactly 0), keeping the swizzled slot of
