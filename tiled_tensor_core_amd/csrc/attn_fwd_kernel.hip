@@ -166,21 +166,6 @@ struct Swz<64> {
   TTC_INLINE static int v(int r) { return 4 * ((r >> 1) & 1); }
 };
 
-// Causal triangle of a 32x32 score block in the transposed accumulator
-// layout: bit l of m[r] is set when lane l's score r (key 8*(r/4) + r%4 +
-// 4*(l/32) of the block) follows the lane's query row (l % 32).
-struct TriLanes {
-  unsigned long long m[16];
-};
-constexpr TriLanes make_tri_lanes() {
-  TriLanes t{};
-  for (int r = 0; r < 16; ++r)
-    for (int l = 0; l < 64; ++l)
-      if (8 * (r >> 2) + (r & 3) + 4 * (l >> 5) > (l & 31)) t.m[r] |= 1ull << l;
-  return t;
-}
-constexpr TriLanes kTriLanes = make_tri_lanes();
-
 // Row reductions across the two lane halves: lanes l and l ^ 32 hold the
 // two halves of one query row.  v_permlane32_swap(x, x) gives lanes 0-31
 // (own, lane + 32) and lanes 32-63 (lane - 32, own), so combining the two
@@ -210,8 +195,7 @@ constexpr int kChunks = 16;    // VALU slices per phase of a pipelined tile
 constexpr int kLoadEvery = 2;  // a pipelined tile issues one K/V tile load every this many steps
 
 // Per-wave state and the work of one key tile.  FIXED: the wave runs in
-// fixed-reference mode (see the kernel), which also keeps fewer registers
-// live (one K read offset instead of one per k-step).
+// fixed-reference mode (see the kernel).
 template <bool BF16, int D, bool FIXED>
 struct Wave {
   using O = Ops<BF16>;
@@ -236,12 +220,7 @@ struct Wave {
   float alpha;       // pending rescale factor of O and l for the current tile
   float mc;          // m * c, the exponent offset of the current tile
   bool moved;        // some row of the wave moved its reference maximum (alpha != 1)
-  // byte offset of this lane's K operand in a K tile, per k-step kk; fixed
-  // mode keeps only k-step 0 and forms kk's as kro[0] ^ 32 kk (the swizzle
-  // index and the chunk 2 kk of the operand share no bits)
-  int kro[FIXED ? 1 : DK];
-  mutable int kcur;  // fixed mode: the offset of the k-step being read (both key blocks use it)
-  mutable int kbase; // fixed mode: an opaque copy of kro[0], taken once per tile
+  int kro[DK];       // byte offset of this lane's K operand in a K tile, per k-step
   int vro[DT];       // byte offset of this lane's V^T operand in a V tile, per d-block
 
   TTC_INLINE static float at(const f32x16 (&s)[KB], int v) { return s[v >> 4][v & 15]; }
@@ -249,21 +228,7 @@ struct Wave {
   // ---- MFMA steps -------------------------------------------------------------
   // Score step i (kk = i / KB, kb = i % KB): S^T[kb] += K[kb-th 32 keys][kk] Q^T.
   TTC_INLINE u32x4 kop(int i, const lds_u8* kt) const {
-    int kr;
-    if constexpr (FIXED) {
-      // an opaque copy per k-step (the reads of a tile come in order, both
-      // key blocks of a k-step together): the compiler must not keep all DK
-      // offsets live
-      if (i == 0) {
-        kbase = kro[0];
-        asm volatile("" : "+v"(kbase));
-      }
-      if (i % KB == 0) kcur = (i / KB) == 0 ? kbase : (kbase ^ (32 * (i / KB)));
-      kr = kcur;
-    } else {
-      kr = kro[i / KB];
-    }
-    return *(const __attribute__((address_space(3))) u32x4*)(kt + kr + (i % KB) * 32 * ROW_BYTES);
+    return *(const __attribute__((address_space(3))) u32x4*)(kt + kro[i / KB] + (i % KB) * 32 * ROW_BYTES);
   }
   TTC_INLINE void qk(int i, u32x4 a, f32x16 (&s)[KB]) const {
     const int kk = i / KB, kb = i % KB;
@@ -299,46 +264,25 @@ struct Wave {
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
   }
   // The causal mask of a tile that starts delta = c0 - wr0 keys after the
-  // wave's first query row (a multiple of 32 for these tile shapes), for a
-  // tile wholly inside the sequence.  delta >= 32: every key follows every
-  // row; delta = 0: block 0 is the triangle, block 1 all future keys;
-  // delta = -32: block 1 is the triangle.  In the triangle, key
-  // 8*(r/4) + r%4 + 4*(lane/32) of the block is hidden from row lane%32 when
-  // it is larger; the lanes that hide score r form a constant mask, and
-  // the score takes one v_cndmask on it.
-  TTC_INLINE static unsigned long long tri_lanes(int r) { return kTriLanes.m[r]; }
-  // Lanes that hide score r of 32-key block kb, whose first key is db =
-  // delta + 32*kb keys after the wave's first row: all (db >= 32), the
-  // triangle (db = 0) or none (db <= -32).  Selected per score, this costs
-  // four scalar instructions a score (the d = 64 steps, short of registers
-  // for the branches of diag_mask8, use it).
-  TTC_INLINE static unsigned long long diag_lanes(int delta, int kb, int r) {
-    const int db = delta + 32 * kb;
-    return db >= 32 ? ~0ull : (db == 0 ? tri_lanes(r) : 0ull);
+  // wave's first query row, for a tile wholly inside the sequence.  Score
+  // e = 16 kb + r of a lane holds key c0 + 32 kb + 8 (r/4) + r%4 + 4 (lane/32)
+  // for query row wr0 + lane % 32; the key is hidden when it follows the row,
+  // that is when rel + 32 kb + 8 (r/4) + r%4 > 0 with the per-lane
+  // rel = delta + 4 (lane/32) - lane % 32: one compare with a constant and
+  // one select per score, and no branch (keys past N follow every row below
+  // N, so this mask hides them as well).
+  TTC_INLINE static int diag_rel(int delta) {
+    const int ln = __lane_id();
+    return delta + 4 * (ln >> 5) - (ln & 31);
   }
-  TTC_INLINE static void diag_mask_one(f32x16 (&s)[KB], int delta, int e) {   // score e = 16*kb + r
+  TTC_INLINE static void diag_mask_one(f32x16 (&s)[KB], int rel, int e) {
     const int kb = e >> 4, r = e & 15;
-    s[kb][r] = __builtin_amdgcn_inverse_ballot_w64(diag_lanes(delta, kb, r)) ? -INFINITY : s[kb][r];
-  }
-  // Scores e0 .. e0+7 (all in 32-key block kb = e0 / 16) under that mask:
-  // one uniform branch picks the block's case, so only a triangle block
-  // pays for its per-score lane masks (about 100 fewer scalar instructions
-  // per masked tile than diag_mask_one).
-  TTC_INLINE static void diag_mask8(f32x16 (&s)[KB], int delta, int e0) {
-    const int kb = e0 >> 4;
-    const int db = delta + 32 * kb;
-    if (db >= 32) {
-#pragma unroll
-      for (int e = e0; e < e0 + 8; ++e) s[kb][e & 15] = -INFINITY;
-    } else if (db == 0) {
-#pragma unroll
-      for (int e = e0; e < e0 + 8; ++e)
-        s[kb][e & 15] = __builtin_amdgcn_inverse_ballot_w64(tri_lanes(e & 15)) ? -INFINITY : s[kb][e & 15];
-    }
+    s[kb][r] = (rel > -(32 * kb + 8 * (r >> 2) + (r & 3))) ? -INFINITY : s[kb][r];
   }
   TTC_INLINE static void diag_mask(f32x16 (&s)[KB], int delta) {
+    const int rel = diag_rel(delta);
 #pragma unroll
-    for (int e0 = 0; e0 < NS; e0 += 8) diag_mask8(s, delta, e0);
+    for (int e = 0; e < NS; ++e) diag_mask_one(s, rel, e);
   }
   // The row's tile maximum mx (both lane halves) moves the reference
   // maximum if some row of the wave outgrew it by the margin (always on the
@@ -437,6 +381,7 @@ struct Wave {
     for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
     float rs[NS / 2], ro[4];
     float mp[10], q[4];
+    int mrel = 0;   // MASKN: the per-lane offset of diag_rel
 #pragma unroll
     for (int g = 0; g < NSTEP; ++g) {
       const bool p1 = g < NQK;
@@ -466,12 +411,9 @@ struct Wave {
         } else {
           const int t = cc / 4 + 1;
           if (MASKN && cc >= 8 && cc < 12) {
-            if constexpr (D == 128) {
-              diag_mask8(sn, mdelta, 8 * (cc - 8));
-            } else {   // (the branches cost the d = 64 step registers it does not have)
+            if (cc == 8) mrel = diag_rel(mdelta);
 #pragma unroll
-              for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
-            }
+            for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mrel, e);
           }
           if (RESCALE && t < DT) {
 #pragma unroll
@@ -542,6 +484,7 @@ struct Wave {
 #pragma unroll
     for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
     float ra = 0.0f, rb = 0.0f, rp = 0.0f;
+    int mrel = 0;   // MASKN: the per-lane offset of diag_rel
 #pragma unroll
     for (int g = 0; g < NSTEP; ++g) {
       const bool p1 = g < NQK;
@@ -564,12 +507,9 @@ struct Wave {
         } else {
           if (cc == 0) pack(s, 15);
           if (MASKN && cc >= 8 && cc < 12) {
-            if constexpr (D == 128) {
-              diag_mask8(sn, mdelta, 8 * (cc - 8));
-            } else {
+            if (cc == 8) mrel = diag_rel(mdelta);
 #pragma unroll
-              for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mdelta, e);
-            }
+            for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mrel, e);
           }
           ra = cc == 0 ? at(s, 0) : ra + at(s, 2 * cc);
           rb = cc == 0 ? at(s, 1) : rb + at(s, 2 * cc + 1);
@@ -779,7 +719,7 @@ attn_fwd_kernel(AttnParams p) {
     const int krow = ln & 31;                     // key row within a 32-key block
     const int kchunk = ln >> 5;                   // + 2*kk
 #pragma unroll
-    for (int kk = 0; kk < (FIXED ? 1 : DK); ++kk)
+    for (int kk = 0; kk < DK; ++kk)
       w.kro[kk] = krow * ROW_BYTES + (((2 * kk + kchunk) ^ S::k(krow)) << 4);
     const int g = ln >> 4, gj = ln & 15;          // 16-lane group for the V reads
     const int vkey = 4 * (g >> 1) + (gj >> 2);    // + 32*kb + 16*h (and + 8)
@@ -818,8 +758,8 @@ attn_fwd_kernel(AttnParams p) {
   const int th1 = p.prio ? tot_tiles / 2 : 0, th2 = p.prio ? (3 * tot_tiles) / 4 : 0,
             th3 = p.prio ? (9 * tot_tiles) / 10 : 0;
   int done_tiles = 0;
-  auto progress = [&]() {
-    ++done_tiles;
+  auto progress = [&](int n) {
+    done_tiles += n;
     if (done_tiles < th1)
       __builtin_amdgcn_s_setprio(3);
     else if (done_tiles < th2)
@@ -998,9 +938,11 @@ attn_fwd_kernel(AttnParams p) {
       }
     };
     constexpr int NL = 2 * PER_W;
+    // (the priority is set once per pair of steps: its branches would
+    // otherwise split the pair's straight-line code in two)
     for (; j + 1 < n_pipe; j += 2) {
+      progress(2);
       wait_all();
-      progress();
       koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)   // no maximum, no rescale
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
@@ -1010,7 +952,6 @@ attn_fwd_kernel(AttnParams p) {
         w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
       ++j;
       wait_all();
-      progress();
       koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sb, sa, K0, V1, ld_odd);
@@ -1022,7 +963,7 @@ attn_fwd_kernel(AttnParams p) {
     }
     if (j < n_pipe) {
       wait_all();
-      progress();
+      progress(1);
       koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
@@ -1054,7 +995,7 @@ attn_fwd_kernel(AttnParams p) {
     };
     for (; j + 1 < n_tiles; ++j) {
       wait_all();
-      progress();
+      progress(1);
       // causal: the next tile may be the last and wholly after this wave's
       // rows (then it is the item's last tile)
       const bool odd = j & 1;
