@@ -10,24 +10,27 @@
 // accumulator in registers before the one write of the output).
 //
 // gfx950 design:
-//   * a workgroup of 4 waves computes a 256 x 256 tile of C; each wave owns
-//     a 128 x 128 quarter as 8 x 8 blocks of v_mfma_f32_16x16x32_bf16
-//     accumulators (256 fp32 per lane, in the accumulation registers).  The
-//     16x16x32 form does the same work per cycle as 32x32x16 but draws less
-//     power on random data, so the power-limited chip keeps a higher clock
-//     (measured: +14 % throughput for back-to-back MFMAs on random bf16).
+//   * a workgroup of 8 waves (two per SIMD) computes a 256 x 256 tile of C;
+//     each wave owns 64 x 128 of it as 4 x 8 blocks of
+//     v_mfma_f32_16x16x32_bf16 accumulators (128 fp32 per lane).  While one
+//     wave of a SIMD issues its loads, LDS writes and fragment reads, the
+//     other keeps the matrix core busy.  The 16x16x32 form does the same
+//     work per cycle as 32x32x16 but draws less power on random data, so the
+//     power-limited chip keeps a higher clock (measured: +14 % throughput for
+//     back-to-back MFMAs on random bf16).
 //   * K advances 64 at a time: A [256 x 64] and W [256 x 64] slices, double-
-//     buffered in LDS.  Each wave moves 16 pieces of 1 KiB per slice
+//     buffered in LDS.  Each wave moves 8 pieces of 1 KiB per slice
 //     (16 bytes per lane) global -> VGPRs -> LDS: it loads the pieces of
 //     slice j+2 during slice j and writes them to LDS during slice j+1, one
-//     piece after every four MFMAs, so the memory instructions never bunch
-//     up (a wave issuing a run of loads stalls its own MFMAs) and every
-//     load keeps a slice of lead.  Loads straight into LDS
-//     (buffer_load ... lds) measured slower here, bunched or spread.
-//   * a slice is two k32 steps of 64 MFMAs.  Step 0 reads step 1's
-//     fragments; step 1 runs 8 MFMAs, waits for the staged pieces and every
-//     wave, then reads the next slice's fragments between its remaining
-//     MFMAs, so no step starts by waiting for LDS.
+//     piece at a time between the MFMAs (A pieces in the slice's first k32
+//     step, W pieces in the second), so every load keeps a slice of lead.
+//     Loads straight into LDS (buffer_load ... lds) measured slower here.
+//   * a k32 step is 8 groups of 4 MFMAs (group nb: W fragment nb against the
+//     wave's 4 A fragments).  W fragments are read two groups ahead, the
+//     next step's A fragments during the step's last groups, so no group
+//     waits for LDS.  The slice's second step, once past its last read of
+//     the slice's buffers, waits for every wave (one barrier per slice) and
+//     then reads the next slice's first fragments.
 //   * an LDS row holds 64 k values (8 chunks of 16 bytes); the chunk index
 //     is XOR-swizzled with (row >> 1) & 7: the 16 lanes of a phase of a
 //     fragment read (rows r .. r+15 at one chunk, 256 bytes of LDS banks)
@@ -41,8 +44,8 @@
 //   * the bias is the accumulators' starting value, so the matrix cores add
 //     the products to it; the epilogue in registers applies GELU (erfc from
 //     Abramowitz and Stegun 7.1.26, rearranged so one form serves both
-//     signs) and rounds to bf16; then each wave stages its 128 x 128 bf16
-//     quarter in LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled with
+//     signs) and rounds to bf16; then each wave stages its 64 x 128 bf16
+//     part in LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled with
 //     row & 15, the 8-byte halves of a chunk swapped in rows with bit 4 set)
 //     and writes C in whole 16-byte pieces, 4 rows of 256 bytes per wave
 //     instruction.
@@ -75,10 +78,10 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #define G_INLINE __device__ __attribute__((always_inline)) inline
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowBytes = kBK * 2;                    // 128 bytes of k per LDS row
 constexpr int kSliceBytes = kBM * kRowBytes;          // 32 KiB per operand slice
-constexpr int kLoadsPerWave = kSliceBytes / (kWaves * 1024);   // 8 per operand
+constexpr int kLoadsPerWave = kSliceBytes / (kWaves * 1024);   // 4 per operand
 constexpr uint32_t kOut = 0x80000000u;                // a buffer offset past any range
 
 static_assert(kSliceBytes % (kWaves * 1024) == 0, "a slice must split evenly over the waves");
@@ -131,7 +134,7 @@ G_INLINE float activation(float z) {
 // inside K and the loads need no per-lane bound check (the k offset of a
 // slice and the row step of a piece are the scalar offset of the load).
 template <int EPI, bool KFULL>
-__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[kSliceBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[kSliceBytes];
@@ -144,7 +147,7 @@ gemm_kernel(GemmParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;             // this wave's quarter of the tile
+  const int wm = wave >> 1, wn = wave & 1;             // this wave's 64 x 128 part of the tile
 
   // ---- tile of this workgroup ---------------------------------------------
   // Workgroups start in index order, dealt round-robin to the 8 XCDs (b % 8),
@@ -176,8 +179,8 @@ gemm_kernel(GemmParams p) {
   const int M = p.M, N = p.N, K = p.K;
 
   // ---- operand loads: HBM -> LDS ----------------------------------------------
-  // Load t of a wave fills LDS bytes [(wave*8 + t) KiB, +1 KiB): chunk index
-  // idx = (wave*8 + t)*64 + lane, row idx / 8, swizzled chunk idx % 8, which
+  // Load t of a wave fills LDS bytes [(wave*4 + t) KiB, +1 KiB): chunk index
+  // idx = (wave*4 + t)*64 + lane, row idx / 8, swizzled chunk idx % 8, which
   // holds logical chunk (idx % 8) ^ ((row >> 1) & 7): k = 8 * that chunk.
   const uint32_t a_rows = (uint32_t)min(kBM, M - m0), w_rows = (uint32_t)min(kBN, N - n0);
   const __amdgpu_buffer_rsrc_t ars = rsrc(p.a + (size_t)m0 * K, a_rows * (uint32_t)K * 2u);
@@ -192,7 +195,7 @@ gemm_kernel(GemmParams p) {
   uint32_t ld_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) ld_off[par] = (uint32_t)(row0 * K + ld_k[par]) * 2u;
-  // A slice moves global -> VGPRs -> LDS: each wave loads its 16 pieces of
+  // A slice moves global -> VGPRs -> LDS: each wave loads its 8 pieces of
   // slice j+2 into registers during slice j and writes them to LDS during
   // slice j+1, so the loads spread over the slice and still have a slice of
   // lead.
@@ -214,9 +217,9 @@ gemm_kernel(GemmParams p) {
   auto swrite = [&](lds_u8* buf, int s, u32x4 v) {
     *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(buf + (wave * kLoadsPerWave + s) * 1024 + lane * 16) = v;
   };
-  // piece q of 16 (0-7 A, 8-15 W): write the staged value into the next
+  // piece q of 8 (0-3 A, 4-7 W): write the staged value into the next
   // slice's buffer, then load the same piece of the slice after it
-  auto stage_piece = [&](lds_u8* nabuf, lds_u8* nwbuf, int q, int k2) {
+  auto stage_piece = [&](lds_u8* nabuf, lds_u8* nwbuf, int q, int k2) __attribute__((always_inline)) {
     if (q < kLoadsPerWave) {
       swrite(nabuf, q, ra[q]);
       ra[q] = gload(ars, q, k2);
@@ -231,12 +234,12 @@ gemm_kernel(GemmParams p) {
   int rd[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rd[ks] = (lane & 15) * kRowBytes + (((4 * ks + (lane >> 4)) ^ ((lane >> 1) & 7)) << 4);
-  const int a_base = wm * 128 * kRowBytes, w_base = wn * 128 * kRowBytes;
+  const int a_base = wm * 64 * kRowBytes, w_base = wn * 128 * kRowBytes;
 
   // Accumulators start at the bias (register r of a lane in column block nb
   // is column nb*16 + 4*(lane / 16) + r, for every row block), so the matrix
   // cores add the products on top and no epilogue add is left.
-  f32x4 acc[8][8];
+  f32x4 acc[4][8];
   {
     const int h4 = 4 * (lane >> 4);
     const __amdgpu_buffer_rsrc_t brs = rsrc(p.bias, EPI != 0 ? (uint32_t)N * 4u : 0u);
@@ -249,58 +252,58 @@ gemm_kernel(GemmParams p) {
         bv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, n < N ? (uint32_t)n * 4u : kOut, 0, 0));
       }
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = bv;
+      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = bv;
     }
   }
 
-  auto read_frags = [&](const lds_u8* abuf, const lds_u8* wbuf, int ks, u32x4 (&af)[8], u32x4 (&wf)[8]) {
-    af[0] = lds_read16(abuf + a_base + rd[ks]);
+  auto rda = [&](const lds_u8* abuf, int ks, int mb) { return lds_read16(abuf + a_base + mb * 16 * kRowBytes + rd[ks]); };
+  auto rdw = [&](const lds_u8* wbuf, int ks, int nb) { return lds_read16(wbuf + w_base + nb * 16 * kRowBytes + rd[ks]); };
+  // A k32 step is 8 groups of 4 MFMAs (group nb: the W fragment nb against
+  // the 4 A fragments).  W fragments are read two groups ahead into a ring of
+  // 4 (8 groups a step keep its places fixed from step to step); the next
+  // step's A fragments go into the other of two A sets during the step's
+  // last groups.  A slice (two steps): step 0 stages the 4 A pieces, one
+  // every other group; step 1 stages the 4 W pieces in groups 0-3 and, after
+  // group 5 (its last reads of this slice's buffers), waits for its LDS
+  // traffic and every wave, then reads the next slice's first fragments
+  // during groups 6 and 7.
+  u32x4 af[2][4], wr[4];
+  auto step = [&](const lds_u8* abuf, const lds_u8* wbuf, int ks, int cur, const lds_u8* nabuf, const lds_u8* nwbuf,
+                  bool last, lds_u8* sabuf, lds_u8* swbuf, int k2) __attribute__((always_inline)) {
+    // on entry: af[cur] holds this step's A fragments, wr[0], wr[1] its W fragments 0 and 1
+    const lds_u8* na = last ? nabuf : abuf;
+    const lds_u8* nw = last ? nwbuf : wbuf;
+    const int nks = last ? 0 : 1;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) wf[nb] = lds_read16(wbuf + w_base + nb * 16 * kRowBytes + rd[ks]);
+    for (int nb = 0; nb < 8; ++nb) {
+      if (last && nb == 6) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the W fragment two groups ahead (this step's, or the next step's 0 and 1)
+      if (nb + 2 < 8) wr[(nb + 2) % 4] = rdw(wbuf, ks, nb + 2);
+      else wr[(nb + 2) % 4] = rdw(nw, nks, nb - 6);
+      // the next step's A fragments, during groups 4-7 (after the barrier when the step is the slice's last)
+      if (nb >= 4 && (!last || nb >= 6)) {
+        if (last) {
+          af[cur ^ 1][2 * (nb - 6)] = rda(na, nks, 2 * (nb - 6));
+          af[cur ^ 1][2 * (nb - 6) + 1] = rda(na, nks, 2 * (nb - 6) + 1);
+        } else {
+          af[cur ^ 1][nb - 4] = rda(na, nks, nb - 4);
+        }
+      }
+      if (ks == 0 && (nb & 1) == 0) stage_piece(sabuf, swbuf, nb >> 1, k2);   // A pieces: every other group of step 0
+      if (ks == 1 && nb < 4) stage_piece(sabuf, swbuf, 4 + nb, k2);           // W pieces: groups 0-3 of step 1
 #pragma unroll
-    for (int mb = 1; mb < 8; ++mb) af[mb] = lds_read16(abuf + a_base + mb * 16 * kRowBytes + rd[ks]);
+      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma(wr[nb % 4], af[cur][mb], acc[mb][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // A slice is two k32 steps of 64 MFMAs.  Step 0 reads step 1's fragments
-  // and stages the next slice's 16 pieces; step 1 runs 8 MFMAs, waits for
-  // the pieces and every wave, then reads the next slice's step-0 fragments
-  // between its remaining 56 MFMAs.
-  u32x4 af0[8], wf0[8];
-  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, lds_u8* nabuf, lds_u8* nwbuf, int k2) {
-    u32x4 af1[8], wf1[8];
-    read_frags(abuf, wbuf, 1, af1, wf1);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) stage_piece(nabuf, nwbuf, q, k2);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma(wf0[nb], af0[mb], acc[mb][nb]);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[0][nb] = mfma(wf1[nb], af1[0], acc[0][nb]);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(nabuf, nwbuf, 0, af0, wf0);
-#pragma unroll
-    for (int mb = 1; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma(wf1[nb], af1[mb], acc[mb][nb]);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  auto compute = [&](const lds_u8* abuf, const lds_u8* wbuf, lds_u8* nabuf, lds_u8* nwbuf, int k2) __attribute__((always_inline)) {
+    step(abuf, wbuf, 0, 0, nabuf, nwbuf, false, nabuf, nwbuf, k2);
+    step(abuf, wbuf, 1, 1, nabuf, nwbuf, true, nabuf, nwbuf, k2);
   };
 
   // ---- main loop: two slices per iteration, one per buffer --------------------
@@ -324,7 +327,10 @@ gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int s2 = 0; s2 < kLoadsPerWave; ++s2) rw[s2] = gload(wrs, s2, kBK);
   __syncthreads();
-  read_frags(A0, W0, 0, af0, wf0);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) af[0][mb] = rda(A0, 0, mb);
+  wr[0] = rdw(W0, 0, 0);
+  wr[1] = rdw(W0, 0, 1);
   for (int j = 0; j < nk; j += 2) {
     compute(A0, W0, A1, W1, (j + 2) * kBK);   // slice j; writes slice j+1, loads slice j+2
     compute(A1, W1, A0, W0, (j + 3) * kBK);   // slice j+1; writes slice j+2, loads slice j+3
@@ -339,9 +345,9 @@ gemm_kernel(GemmParams p) {
 
   // ---- epilogue -------------------------------------------------------------
   // Lane l holds, for block (mb, nb), row m = mb*16 + l % 16 of the wave's
-  // quarter and columns nb*16 + 4*(l / 16) + r for register r.  Each wave
-  // stages its quarter in one 32 KiB LDS object.
-  lds_u8* const stage = wave == 0 ? A0 : wave == 1 ? W0 : wave == 2 ? A1 : W1;
+  // 64 x 128 part and columns nb*16 + 4*(l / 16) + r for register r.  Each
+  // wave stages its part in one half of a 32 KiB LDS object.
+  lds_u8* const stage = (wave >> 1 == 0 ? A0 : wave >> 1 == 1 ? W0 : wave >> 1 == 2 ? A1 : W1) + (wave & 1) * 16384;
   // the lane index again, from the execution mask (all lanes are active),
   // so no register holds it through the loop and the epilogue's addresses
   // are computed here
@@ -351,7 +357,7 @@ gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < 4; ++mb) {
       const int row = mb * 16 + ml;
       const float v0 = activation<EPI>(acc[mb][nb][0]);
       const float v1 = activation<EPI>(acc[mb][nb][1]);
@@ -372,11 +378,11 @@ gemm_kernel(GemmParams p) {
   const int c = el & 15;
   const int n = n0 + wn * 128 + c * 8;
 #pragma unroll
-  for (int it = 0; it < 32; ++it) {
+  for (int it = 0; it < 16; ++it) {
     const int row = it * 4 + (el >> 4);
     u32x4 v = lds_read16(stage + row * 256 + ((c ^ (row & 15)) << 4));
     if ((it >> 2) & 1) v = (u32x4){v[2], v[3], v[0], v[1]};   // rows with bit 4 set hold their halves swapped
-    const uint32_t off = n < N ? ((uint32_t)(wm * 128 + row) * (uint32_t)N + (uint32_t)n) * 2u : kOut;
+    const uint32_t off = n < N ? ((uint32_t)(wm * 64 + row) * (uint32_t)N + (uint32_t)n) * 2u : kOut;
     __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, 0);
   }
 }
