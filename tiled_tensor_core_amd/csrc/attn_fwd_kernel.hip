@@ -28,12 +28,13 @@
 //   * software pipeline inside every wave, scheduled by hand: one tile is 32
 //     steps (d = 128; 16 for d = 64), each one MFMA, the LDS reads of the
 //     MFMA a few steps ahead, and a fixed slice of VALU work.  While the
-//     MFMAs compute the scores of tile j+1, the VALU turns tile j's scores
-//     into probabilities; while the MFMAs accumulate P_j V_j, the VALU
-//     rescales O just ahead of them, sums the row and finds the maximum of
-//     tile j+1.  A scheduling fence closes every step so the compiler keeps
-//     this order; the K stream runs one tile ahead of the V stream and there
-//     is one barrier per tile.
+//     MFMAs compute the scores of tile j+1, the VALU turns most of tile j's
+//     scores into probabilities; while the MFMAs accumulate P_j V_j, the
+//     VALU finishes them, sums the row and (running-maximum mode) rescales O
+//     just ahead of the MFMAs and finds the maximum of tile j+1.  A
+//     scheduling fence closes every step so the compiler keeps this order;
+//     the K stream runs one tile ahead of the V stream and there is one
+//     barrier per tile.
 //   * scores are computed transposed, S^T = K Q^T, so the accumulator puts
 //     one query row per lane (column = lane % 32) and 16 of its keys in the
 //     lane's registers; the other 16 keys of that row sit in lane ^ 32.  A
@@ -235,9 +236,13 @@ struct Wave {
     s[kb] = O::mfma(a, qf[kk], kk == 0 ? (f32x16){} : s[kb]);
   }
   // P V step i (t = i / (2 KB), kb = (i / 2) % KB, h = i % 2):
-  // O^T[t] += V^T[t-th 32 dims][16 keys] P^T[16 keys].
+  // O^T[t] += V^T[t-th 32 dims][16 keys] P^T[16 keys].  KBM: the steps run
+  // key-block-major instead (kb = i / (2 DT), t = (i / 2) % DT), so the first
+  // half of them needs only the first key block's P; every O^T[t] still
+  // takes its four products in the same order.
+  template <bool KBM = false>
   TTC_INLINE u32x4 vop(int i, const lds_u8* vt) const {
-    const int t = i / (2 * KB), kb = (i / 2) % KB, h = i % 2;
+    const int t = KBM ? (i / 2) % DT : i / (2 * KB), kb = KBM ? i / (2 * DT) : (i / 2) % KB, h = i % 2;
     const lds_u8* pa = vt + vro[t] + (kb * 32 + 16 * h) * ROW_BYTES;
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
@@ -247,8 +252,9 @@ struct Wave {
                    __builtin_bit_cast(uint32_t, (i16x2){hi[0], hi[1]}),
                    __builtin_bit_cast(uint32_t, (i16x2){hi[2], hi[3]})};
   }
+  template <bool KBM = false>
   TTC_INLINE void pv(int i, u32x4 a) {
-    const int t = i / (2 * KB), kb = (i / 2) % KB, h = i % 2;
+    const int t = KBM ? (i / 2) % DT : i / (2 * KB), kb = KBM ? i / (2 * DT) : (i / 2) % KB, h = i % 2;
     oacc[t] = O::mfma(a, pb[kb][h], oacc[t]);
   }
 
@@ -466,15 +472,19 @@ struct Wave {
 
   // ---- one pipelined tile with a fixed exponent reference ---------------------
   // The step of fixed-reference mode: as pipe_tile, but no maximum, no
-  // rescale, and a schedule that spreads the VALU work evenly over the steps
-  // and keeps three running sums instead of a reduction tree:
-  //   phase 1 (scores of tile j+1), slice cc: p = exp2(s*c - mc) of scores
-  //     2cc, 2cc+1; pack of scores 2cc-2, 2cc-1 (cc >= 1)
-  //   phase 2 (O^T += V^T P^T), slice cc: pack of scores 30, 31 (cc = 0; the
-  //     P V step that reads it is the fourth); scores 2cc, 2cc+1 into two
-  //     chains of l; packed dword cc into the chain of lo; at cc = 15 both
-  //     sums join l and lo.  MASKN: the causal mask of tile j+1 in slices
-  //     8-11, as in pipe_tile.
+  // rescale, and a schedule that spreads the VALU work evenly over the two
+  // phases (an exponential costs twice an FMA, so a phase doing all 32
+  // would carry most of the step's VALU time) and keeps running sums instead
+  // of a reduction tree.  The P V steps run key-block-major, so the second
+  // key block's P is needed only halfway through phase 2:
+  //   phase 1 (scores of tile j+1): p = exp2(s*c - mc) of scores 0-23, two
+  //     and one in alternate slices; each pair packed a slice after it
+  //   phase 2 (O^T += V^T P^T), slices 0-7: p of scores 24-31, one a slice,
+  //     and the packs of scores 22-29; slice 8: the pack of scores 30, 31
+  //     (read by the P V step after it); slices 8-15: all 32 p into four
+  //     chains of l; every slice: packed dword cc into the chain of lo; at
+  //     cc = 15 the sums join l and lo.  MASKN: the causal mask of tile j+1
+  //     in slices 8-11, as in pipe_tile.
   template <int NLOAD, class LD, bool MASKN = false>
   TTC_INLINE void pipe_tile_fixed(f32x16 (&s)[KB], f32x16 (&sn)[KB], const lds_u8* kt, const lds_u8* vt,
                                   const LD& ld, int mdelta = 0) {
@@ -483,39 +493,57 @@ struct Wave {
     u32x4 op[L];
 #pragma unroll
     for (int g = 0; g < L; ++g) op[g] = kop(g, kt);
-    float ra = 0.0f, rb = 0.0f, rp = 0.0f;
+    float ra = 0.0f, rb = 0.0f, rc = 0.0f, rd = 0.0f, rp = 0.0f;
     int mrel = 0;   // MASKN: the per-lane offset of diag_rel
+    // probabilities done after phase-1 slice cc: 2, 3, 5, 6, ..., 24
+    auto done1 = [](int cc) { return cc < 0 ? 0 : (3 * (cc + 1) + 1) / 2; };
 #pragma unroll
     for (int g = 0; g < NSTEP; ++g) {
       const bool p1 = g < NQK;
       const int i = p1 ? g : g - NQK;
       const u32x4 a = op[g % L];
-      if (g + L < NSTEP) op[g % L] = (g + L < NQK) ? kop(g + L, kt) : vop(g + L - NQK, vt);
+      if (g + L < NSTEP) op[g % L] = (g + L < NQK) ? kop(g + L, kt) : vop<true>(g + L - NQK, vt);
       if (p1)
         qk(i, a, sn);
       else
-        pv(i, a);
+        pv<true>(i, a);
       if (g % kLoadEvery == 0 && g / kLoadEvery < NLOAD) ld(g / kLoadEvery);
       const int n_steps = p1 ? NQK : NPV;
       const int c_lo = i * kChunks / n_steps, c_hi = (i + 1) * kChunks / n_steps;
 #pragma unroll
       for (int cc = c_lo; cc < c_hi; ++cc) {
         if (p1) {
-          prob(s, 2 * cc);
-          prob(s, 2 * cc + 1);
-          if (cc >= 1) pack(s, cc - 1);
+          // probabilities 0-23, one or two a slice; each pack a slice after its pair
+#pragma unroll
+          for (int v = done1(cc - 1); v < done1(cc); ++v) prob(s, v);
+#pragma unroll
+          for (int k = done1(cc - 2) / 2; k < done1(cc - 1) / 2; ++k) pack(s, k);
         } else {
-          if (cc == 0) pack(s, 15);
+          // slices 0-7 (the first key block's P V): probabilities 24-31,
+          // packs 11-14 and the packed sum of key block 0; slices 8-15: the
+          // sums of all 32 probabilities, pack 15, the packed sum of key block 1
+          if (cc < 8) {
+            prob(s, 24 + cc);
+            if (cc == 0) pack(s, 11);
+            if (cc >= 2 && (cc & 1) == 0) pack(s, 11 + cc / 2);
+          } else if (cc == 8) {
+            pack(s, 15);
+          }
           if (MASKN && cc >= 8 && cc < 12) {
             if (cc == 8) mrel = diag_rel(mdelta);
 #pragma unroll
             for (int e = 8 * (cc - 8); e < 8 * (cc - 8) + 8; ++e) diag_mask_one(sn, mrel, e);
           }
-          ra = cc == 0 ? at(s, 0) : ra + at(s, 2 * cc);
-          rb = cc == 0 ? at(s, 1) : rb + at(s, 2 * cc + 1);
+          if (cc >= 8) {
+            const int v0 = 4 * (cc - 8);
+            ra = cc == 8 ? at(s, v0) : ra + at(s, v0);
+            rb = cc == 8 ? at(s, v0 + 1) : rb + at(s, v0 + 1);
+            rc = cc == 8 ? at(s, v0 + 2) : rc + at(s, v0 + 2);
+            rd = cc == 8 ? at(s, v0 + 3) : rd + at(s, v0 + 3);
+          }
           rp = O::sum2(pb[cc >> 3][(cc >> 2) & 1][cc & 3], rp);
           if (cc == 15) {
-            l += ra + rb;
+            l += (ra + rb) + (rc + rd);
             lo += rp;
           }
         }
