@@ -707,16 +707,15 @@ attn_fwd_kernel(AttnParams p) {
   };
   int koff, voff;
   lane_offsets(lane, koff, voff);
-  // lane offset of K load t (an opaque copy, so the compiler does not keep
-  // all PER_W of them live across the loop)
-  int kload = 0;   // an opaque copy of koff, taken once per step (at piece 0)
-  auto koff_t = [&](int t) {
-    if (t == 0) {
-      kload = koff;
-      asm volatile("" : "+v"(kload));
-    }
-    return t == 0 ? kload : (kload ^ (64 * t));
+  // lane offset of K load t, kept for the whole item (four VGPRs instead of
+  // an XOR per load)
+  int kofs[PER_W];
+  auto set_kofs = [&]() {
+#pragma unroll
+    for (int t = 0; t < PER_W; ++t) kofs[t] = koff ^ (64 * t);
   };
+  set_kofs();
+  auto koff_t = [&](int t) { return kofs[t]; };
   // The last tile's rows past N (if any) repeat row N-1 (finite values whose
   // scores are masked, so they add exactly 0), keeping the swizzled slot of
   // the row they stand in for.
@@ -830,6 +829,7 @@ attn_fwd_kernel(AttnParams p) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       lane_offsets(ln, koff, voff);
+      set_kofs();
       read_offsets(ln);
     }
     // the item's loads have landed, and every wave is done with the previous
@@ -946,21 +946,23 @@ attn_fwd_kernel(AttnParams p) {
     // V_{j+1} into the other V buffer, both wholly inside the sequence, one
     // 1 KiB piece at a time.  Even j: K_{j+1} is in K1, V_j in V0.
     // When step j has no K_{j+2} (the last step of an item whose tiles all
-    // run here), its K loads still issue, sent out of range through the lane
-    // offset (the part of the address the buffer's range check covers): no
-    // memory is read, and the step needs no branch per load.
+    // run here), its K loads still issue, through a copy of the K buffer
+    // resource that spans no bytes: every access is out of range, no memory
+    // is read, and the step needs no branch and no VALU per load.
     int j = 0;
-    int koob = 0;   // 0, or an offset past the head for the K loads of this step
+    // the K loads of a step with no K_{j+2} go through a buffer of no bytes
+    const u32x4 krs_void = (u32x4){krs[0], krs[1], 0u, krs[3]};
+    u32x4 kstep = krs;
     auto ld_even = [&](int k) {
       if (k < PER_W) {
-        load_one(krs, K0 + wofs + k * 1024, koff_t(k) | koob, (j + 2) * TILE_BYTES + k * 1024);
+        load_one(kstep, K0 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
       } else {
         load_one(vrs, V1 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
     };
     auto ld_odd = [&](int k) {
       if (k < PER_W) {
-        load_one(krs, K1 + wofs + k * 1024, koff_t(k) | koob, (j + 2) * TILE_BYTES + k * 1024);
+        load_one(kstep, K1 + wofs + k * 1024, koff_t(k), (j + 2) * TILE_BYTES + k * 1024);
       } else {
         load_one(vrs, V0 + wofs + (k - PER_W) * 1024, voff, (j + 1) * TILE_BYTES + (k - PER_W) * 1024);
       }
@@ -971,7 +973,7 @@ attn_fwd_kernel(AttnParams p) {
     for (; j + 1 < n_pipe; j += 2) {
       progress(2);
       wait_all();
-      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
+      kstep = j + 2 < n_tiles ? krs : krs_void;
       if constexpr (FIXED)   // no maximum, no rescale
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
       else if (w.moved)
@@ -980,7 +982,7 @@ attn_fwd_kernel(AttnParams p) {
         w.template pipe_tile<false, NL>(sa, sb, K1, V0, ld_even);
       ++j;
       wait_all();
-      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
+      kstep = j + 2 < n_tiles ? krs : krs_void;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sb, sa, K0, V1, ld_odd);
       else if (w.moved)
@@ -992,7 +994,7 @@ attn_fwd_kernel(AttnParams p) {
     if (j < n_pipe) {
       wait_all();
       progress(1);
-      koob = j + 2 < n_tiles ? 0 : (int)0x80000000;
+      kstep = j + 2 < n_tiles ? krs : krs_void;
       if constexpr (FIXED)
         w.template pipe_tile_fixed<NL>(sa, sb, K1, V0, ld_even);
       else if (w.moved)
@@ -1011,9 +1013,9 @@ attn_fwd_kernel(AttnParams p) {
     auto ld_any = [&](int k) {
       const bool odd = j & 1;
       if (k < PER_W) {
-        // no K_{j+2}: the loads go out of range, as in the pipelined steps
-        const int oob = j + 2 < n_tiles ? 0 : (int)0x80000000;
-        load_one(krs, (odd ? K1 : K0) + wofs + k * 1024, (koff_t(k) + (j + 2 == j_tail ? tail_delta(k) : 0)) | oob,
+        // no K_{j+2}: the loads go through the empty resource, as in the pipelined steps
+        load_one(j + 2 < n_tiles ? krs : krs_void, (odd ? K1 : K0) + wofs + k * 1024,
+                 koff_t(k) + (j + 2 == j_tail ? tail_delta(k) : 0),
                  (j + 2) * TILE_BYTES + k * 1024);
       } else {
         const int t = k - PER_W;
