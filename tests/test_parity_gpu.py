@@ -74,6 +74,35 @@ def test_batch_head_mapping(B, H):
         full_check(q, k, v, "bf16", causal, 0.125, tag=f"B={B} H={H} causal={causal}")
 
 
+# ---- seeded random configurations ----------------------------------------------
+
+def _random_case(i):
+    """Configuration i of a fixed, seeded draw: batch, heads, a length from 1
+    to 600 (most not a multiple of the 64-key tile), head dim, dtype, mask,
+    the value distribution of Q and K, and the scale (a multiple of
+    1/sqrt(d), negative in some cases)."""
+    rng = np.random.default_rng(1000 + i)
+    B = int(rng.integers(1, 4))
+    H = int(rng.integers(1, 6))
+    N = int(rng.integers(1, 601))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    causal = bool(rng.integers(0, 2))
+    kind = str(rng.choice(["normal", "uniform"]))
+    std = float(rng.choice([0.5, 1.0, 2.0, 3.0]))
+    scale = float(rng.choice([0.5, 1.0, 2.0, -1.0])) / float(np.sqrt(d))
+    return B, H, N, d, dtype, causal, kind, std, scale
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(i):
+    B, H, N, d, dtype, causal, kind, std, scale = _random_case(i)
+    qk = synth.Dist(kind, std)
+    q, k, v = synth.make_qkv(B, H, N, d, dtype, qk, qk, synth.Dist("normal", 1.0), seed=2000 + i)
+    full_check(q, k, v, dtype, causal, scale,
+               tag=f"case {i}: B={B} H={H} N={N} d={d} {dtype} causal={causal} {kind}({std}) scale={scale:.4g}")
+
+
 # ---- scale and value edge cases -----------------------------------------------
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1e-30, 2.0, -1.5])
