@@ -67,6 +67,22 @@ def test_parity(M, N, K, epi):
            f"{M}x{N}x{K} epi={epi}")
 
 
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes(i):
+    """Seeded random shapes: M 1-700, N and K multiples of 8 up to 704 (K a
+    multiple of 128 in some draws, the path without load bound checks), and
+    a random epilogue."""
+    rng = np.random.default_rng(3000 + i)
+    M = int(rng.integers(1, 701))
+    N = 8 * int(rng.integers(1, 89))
+    K = 128 * int(rng.integers(1, 6)) if rng.integers(0, 3) == 0 else 8 * int(rng.integers(1, 89))
+    epi = int(rng.choice([EPI_NONE, EPI_BIAS, EPI_BIAS_GELU]))
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=4000 + i)
+    c = _run(a, w, b, epi)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), epi,
+           f"case {i}: {M}x{N}x{K} epi={epi}")
+
+
 def test_many_tiles_every_element():
     """342 tiles of 256 x 256 (one full window of 256 concurrently running
     tiles and a partial one, ragged in M and N): every element against the
