@@ -697,7 +697,7 @@ attn_fwd_kernel(AttnParams p) {
   // load t fetches at the lane offset of load 0 plus 1 KiB * t; the K swizzle
   // adds 4t to the swizzle index (both head dims), so K load t fetches at
   // (lane offset of load 0) ^ 64t, plus 1 KiB * t.  The 1 KiB * t goes into
-  // the scalar offset: one VGPR each for all K and all V loads.
+  // the scalar offset: one VGPR for all V loads, one per K load.
   const int first_idx = wave * PER_W * 64 + lane;   // LDS chunk index of this lane's first load
   auto lane_offsets = [&](int ln, int& ko, int& vo) {
     const int idx = wave * PER_W * 64 + ln;
