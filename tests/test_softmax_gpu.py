@@ -80,6 +80,20 @@ def test_shapes(dtype, rows, cols):
     check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"{dtype} {rows}x{cols}")
 
 
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes(i):
+    """Seeded random row counts (1-300), widths (1-20000, every alignment),
+    dtypes and value spreads (std 0.5-8)."""
+    rng = np.random.default_rng(5000 + i)
+    rows = int(rng.integers(1, 301))
+    cols = int(rng.integers(1, 20001))
+    dtype = str(rng.choice(["fp32", "bf16", "fp16"]))
+    std = float(rng.choice([0.5, 1.0, 3.0, 8.0]))
+    x = synth.make_softmax_input(rows, cols, dtype, dist=synth.Dist("normal", std), seed=6000 + i)
+    y = run_gpu(x, dtype)
+    check(y, softmax_rows_ref(synth.softmax_to_f64(x, dtype)), dtype, f"case {i}: {dtype} {rows}x{cols} std {std}")
+
+
 ODD_COLS = {  # byte lengths that are not multiples of 16; the last ones pass 16 KiB (element-wise path)
     "fp16": [1, 3, 7, 9, 15, 17, 63, 65, 129, 513, 1001, 1023, 2047, 4095, 8191, 8193, 12345],
     "bf16": [1, 5, 8, 17, 255, 1001, 2049, 8191, 8193],
