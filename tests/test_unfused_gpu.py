@@ -65,6 +65,24 @@ def test_mid_workload(causal):
     _check(q, k, v, w.dtype, causal, w.scale, f"unfused mid causal={causal}", probs=False)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_configurations(i):
+    """Seeded random batch, heads, lengths (1-400), head dims, dtypes, masks,
+    Q/K spreads and signed scales; O, LSE and the probability matrix."""
+    rng = np.random.default_rng(7000 + i)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    N = int(rng.integers(1, 401))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    causal = bool(rng.integers(0, 2))
+    std = float(rng.choice([0.5, 1.0, 2.0]))
+    scale = float(rng.choice([0.5, 1.0, -1.0])) / float(np.sqrt(d))
+    qk = synth.Dist("normal", std)
+    q, k, v = synth.make_qkv(B, H, N, d, dtype, qk, qk, synth.Dist("normal", 1.0), seed=8000 + i)
+    _check(q, k, v, dtype, causal, scale,
+           f"unfused case {i}: B={B} H={H} N={N} d={d} {dtype} causal={causal} std {std} scale {scale:.4g}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
