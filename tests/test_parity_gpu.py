@@ -249,6 +249,50 @@ def test_peaky_long_rows_both_modes(mode):
 
 # ---- exact properties the mathematics fixes ---------------------------------------
 
+@pytest.mark.slow
+def test_longest_sequence_closed_form():
+    """The longest length the boundary admits at d = 128, N = 2^23 - 129
+    (its fp32 O head plus 128 rows just fits 32-bit offsets; the last
+    128-row block is ragged by one row), causal, one head.  K = 0, so every
+    visible key weighs the same, and V[j, c] = ((7 j + 13 c) mod 256 - 128) / 64
+    (exact in bf16).  Then O[i] is the mean of V[0..i], in closed form from
+    the 256-key period of V (7 is odd, so a period holds every residue once
+    and sums to -2 in every column), and LSE[i] = ln(i + 1).  Checked on rows
+    at the start, at period edges and at the end, where the O store offsets
+    come within 2^16 of 2^32; no row may be left unwritten."""
+    import torch
+
+    from tiled_tensor_core_amd import attn
+
+    N, d = (1 << 23) - 129, 128
+    dev = "cuda"
+    q = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros_like(q)
+    j = torch.arange(N, device=dev, dtype=torch.int32)[:, None]
+    c = torch.arange(d, device=dev, dtype=torch.int32)[None, :]
+    v = ((((7 * j + 13 * c) % 256) - 128).to(torch.float32) / 64).to(torch.bfloat16).view(1, 1, N, d)
+    del j, c
+    o = torch.full((1, 1, N, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((1, 1, N), float("nan"), dtype=torch.float32, device=dev)
+    print(f"[case] longest sequence N={N} d={d} causal", flush=True)
+    attn.attn_fwd(q, k, v, o, lse, 1, 1, N, d, 1, d ** -0.5)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(o).any()) and not bool(torch.isnan(lse).any()), "a row was left unwritten"
+    rows = np.array([0, 1, 2, 255, 256, 257, 4095, 1000003, N // 2, N - 257, N - 129, N - 128, N - 2, N - 1])
+    rows = np.unique(np.concatenate([rows, np.random.default_rng(9).integers(0, N, 20)]))
+    cc = np.arange(d)
+    got_o = o[0, 0, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    got_l = lse[0, 0, torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    for idx, i in enumerate(rows):
+        n = int(i) + 1
+        per, rem = divmod(n, 256)
+        part = (((7 * np.arange(rem)[:, None] + 13 * cc[None, :]) % 256) - 128).sum(axis=0) / 64.0
+        ref = (per * -2.0 + part) / n
+        err_o = float(np.max(np.abs(got_o[idx] - ref)))
+        err_l = abs(got_l[idx] - np.log(n))
+        assert err_o <= 1e-3 and err_l <= 1e-4, f"row {i}: O error {err_o:.3e}, LSE error {err_l:.3e}"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_first_causal_row_is_v0(dtype, d):
