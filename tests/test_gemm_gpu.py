@@ -83,6 +83,18 @@ def test_random_shapes(i):
            f"case {i}: {M}x{N}x{K} epi={epi}")
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 8, 4194296), (5, 8, 4194176), (8, 4194296, 8)])
+def test_largest_dimensions(M, N, K):
+    """N and K at the boundary's limit (4194296: 256 rows of them in bf16 fit
+    the 2^31-byte range of a tile's buffer) or the largest multiple of 128
+    below it (the path without load bound checks): every element against the
+    oracle."""
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=K + N)
+    c = _run(a, w, b, EPI_BIAS_GELU)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
+           f"{M}x{N}x{K} at the size limit")
+
+
 def test_many_tiles_every_element():
     """342 tiles of 256 x 256 (one full window of 256 concurrently running
     tiles and a partial one, ragged in M and N): every element against the
