@@ -338,6 +338,36 @@ def test_equal_keys_uniform_weights():
         np.testing.assert_allclose(lse.cpu().numpy(), s + np.log(n), rtol=0, atol=1e-4)
 
 
+# ---- non-finite inputs -------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nan_inputs_follow_the_definition(dtype, d, causal):
+    """A NaN in one key row reaches every query row that sees that key (all
+    rows; causal: the rows at and after it) and no other; a NaN in one query
+    row reaches that row only.  The NaN rows of O and LSE are exactly the
+    oracle's (softmax of a row holding NaN is NaN), and the other rows meet
+    the usual tolerances, although the item holding them is computed again."""
+    B, H, N = 1, 2, 300
+    q, k, v = _bits((B, H, N, d), dtype, seed=d + int(causal))
+    nan_bits = np.uint16(0x7FC0 if dtype == "bf16" else 0x7E00)
+    k[0, 0, 137, :] = nan_bits
+    q[0, 1, 200, 5] = nan_bits
+    o, lse = run_hip(q, k, v, dtype, causal, 1 / np.sqrt(d))
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = attention_ref(synth.bits_to_f64(q, dtype), synth.bits_to_f64(k, dtype),
+                                   synth.bits_to_f64(v, dtype), causal, 1 / np.sqrt(d))
+    nan_rows = np.isnan(lse_ref)
+    assert nan_rows.any() and not nan_rows.all()
+    assert np.array_equal(np.isnan(lse), nan_rows), "LSE NaN rows differ from the oracle's"
+    assert np.array_equal(np.isnan(o).any(axis=-1), nan_rows), "O NaN rows differ from the oracle's"
+    assert np.array_equal(np.isnan(o).all(axis=-1), nan_rows), "a NaN row of O is only partly NaN"
+    fin = ~nan_rows
+    assert_close(o[fin][None], lse[fin][None], o_ref[fin][None], lse_ref[fin][None],
+                 tag=f"finite rows {dtype} d={d} causal={causal}")
+
+
 # ---- memory behaviour ------------------------------------------------------------
 
 def test_writes_every_row_and_nothing_else():
