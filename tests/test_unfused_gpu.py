@@ -65,6 +65,29 @@ def test_mid_workload(causal):
     _check(q, k, v, w.dtype, causal, w.scale, f"unfused mid causal={causal}", probs=False)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nan_inputs_follow_the_definition(dtype, causal):
+    """As for the fused kernel: a NaN in one key row reaches exactly the query
+    rows that see it, a NaN in one query row only that row."""
+    B, H, N, d = 1, 2, 300, 64
+    q, k, v = synth.make_qkv(B, H, N, d, dtype, seed=11 + int(causal))
+    nan_bits = np.uint16(0x7FC0 if dtype == "bf16" else 0x7E00)
+    k[0, 0, 137, :] = nan_bits
+    q[0, 1, 200, 5] = nan_bits
+    o, lse, _ = _run(q, k, v, dtype, causal, 0.125)
+    q64, k64, v64 = (synth.bits_to_f64(x, dtype) for x in (q, k, v))
+    o_ref, l_ref = attention_ref(q64, k64, v64, causal, 0.125)
+    nan_rows = np.isnan(l_ref)
+    assert nan_rows.any() and not nan_rows.all()
+    assert np.array_equal(np.isnan(lse), nan_rows), "LSE NaN rows differ from the oracle's"
+    assert np.array_equal(np.isnan(o).any(axis=-1), nan_rows), "O NaN rows differ from the oracle's"
+    assert np.array_equal(np.isnan(o).all(axis=-1), nan_rows), "a NaN row of O is only partly NaN"
+    fin = ~nan_rows
+    assert_close(o[fin][None], lse[fin][None], o_ref[fin][None], l_ref[fin][None],
+                 tag=f"unfused finite rows {dtype} causal={causal}")
+
+
 @pytest.mark.parametrize("i", range(8))
 def test_random_configurations(i):
     """Seeded random batch, heads, lengths (1-400), head dims, dtypes, masks,
