@@ -88,6 +88,66 @@ def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
 WARMUP_MIN_S = 0.5
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock every ``period`` seconds on a
+    background thread while the timed loops run, as context beside the
+    timings (the chip is power-bound, and boxes hold different clocks under
+    load).  The clock is the starred level of the amdgpu driver's
+    ``pp_dpm_sclk`` file (deep-sleep readings, marked ``S:``, are skipped); the
+    summary is None where no such file is readable.  Only the host reads a
+    file here; nothing is launched on the GPU."""
+
+    def __init__(self, period=0.001):
+        import glob
+
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if "*" in line and not line.lstrip().startswith("S:"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self.path is not None:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples, dtype=np.float64)
+        return {"median": float(np.median(v)), "min": float(v.min()), "max": float(v.max()),
+                "samples": int(v.size), "source": self.path}
+
+
 def warm_up(torch, launch, warmup, min_seconds=WARMUP_MIN_S):
     """Run ``warmup`` untimed launches, and more until ``min_seconds`` of
     wall time have passed with the GPU busy (synchronising every 8 launches,
@@ -113,19 +173,20 @@ def time_launches(torch, launch, stream, steps, warmup, warmup_s=WARMUP_MIN_S):
     warm_up(torch, launch, warmup, warmup_s)
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
-    t_all0.record(stream)
-    for _ in range(steps):
-        launch()
-    t_all1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_all0.elapsed_time(t_all1)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t_all0.record(stream)
+        for _ in range(steps):
+            launch()
+        t_all1.record(stream)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
     per = sorted(st.elapsed_time(e) for st, e in zip(starts, ends))
     return {
         "ms_per_step": total_ms / steps,
@@ -133,6 +194,7 @@ def time_launches(torch, launch, stream, steps, warmup, warmup_s=WARMUP_MIN_S):
         "kernel_ms_median": float(np.median(per)),
         "kernel_ms_min": float(per[0]),
         "kernel_ms_p90": float(np.percentile(per, 90)),
+        "sclk_mhz": clk.summary(),
     }
 
 
@@ -269,6 +331,7 @@ def run_softmax(a, torch, attn, synth):
         "config": {"workload": f"row softmax {w.name} {w.describe()}", "rows": w.rows, "cols": w.cols,
                    "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -375,6 +438,7 @@ def run_gemm(a, torch, attn, synth):
         "config": {"workload": f"gemm + bias + gelu {wl.name} {wl.describe()}", "M": wl.M, "N": wl.N, "K": wl.K,
                    "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -467,6 +531,7 @@ def run_unfused(a, torch, attn, synth):
             "parallelism": "none (1 GPU)",
         },
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -671,6 +736,7 @@ def main():
             "launch": (f"tuned {list(cfg.as_tuple())}" if cfg is not None else "built-in"),
         },
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -694,6 +760,7 @@ def main():
             "ms_per_step": round(rn["ms_per_step"], 5),
             "kernel_ms_mean": round(rn["kernel_ms_mean"], 5),
             "frac": round(rn["flops"] / (rn["kernel_ms_mean"] * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+            "sclk_mhz": rn["sclk_mhz"],
             "workload": f"attention fwd non-causal {w.describe()}",
         }
         print("[bench] timed the non-causal mask", file=sys.stderr, flush=True)
