@@ -633,7 +633,8 @@ def run_split(a, torch, attn, synth):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    # 700 steps: over 200 ms of timed launches on the default workload (about 0.3 ms each)
+    ap.add_argument("--steps", type=int, default=700)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama")
     ap.add_argument("--kernel", choices=["attention", "softmax", "gemm", "unfused"], default="attention",
