@@ -74,6 +74,17 @@ def test_batch_head_mapping(B, H):
         full_check(q, k, v, "bf16", causal, 0.125, tag=f"B={B} H={H} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype", [(7, 10001, 5, 64, "bf16"), (5, 411, 130, 128, "fp16")])
+def test_many_heads(B, H, N, d, dtype):
+    """Far more items than resident workgroups: 70007 one-block heads (B*H
+    above 2^16, not a multiple of 8, so the last group of heads is partial),
+    and 2055 heads of two blocks each, the second ragged; every row of every
+    head against the oracle, both masks."""
+    q, k, v = _bits((B, H, N, d), dtype, seed=B + H + N)
+    for causal in (False, True):
+        full_check(q, k, v, dtype, causal, 1 / np.sqrt(d), tag=f"B={B} H={H} N={N} d={d} causal={causal}")
+
+
 # ---- seeded random configurations ----------------------------------------------
 
 def _random_case(i):
