@@ -106,6 +106,20 @@ def test_many_tiles_every_element():
            f"{M}x{N}x{K} every element")
 
 
+@pytest.mark.parametrize("M,N,K", [(2049, 4088, 1024), (1000, 776, 384)])
+def test_ragged_tiles_without_k_checks(M, N, K):
+    """K a multiple of 128 (loads without k checks), M and N ragged: the
+    last tile row holds one row of A (2049 = 8 * 256 + 1), the last tile
+    column 248 rows of W, over 128 tiles of 256 x 256 (the main kernel) and,
+    second shape, under (the small-problem kernel).  The rows of a piece past
+    M or N must fall outside the tile's buffer range (the range check covers
+    the lane offset only); every element against the oracle."""
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=M + K)
+    c = _run(a, w, b, EPI_BIAS_GELU)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
+           f"{M}x{N}x{K} ragged, no k checks")
+
+
 def test_gelu_range_and_large_values():
     """Pre-activations from -40 to 40 (scaled weights): both GELU tails and the
     region around 0, where GELU bends, are exercised."""

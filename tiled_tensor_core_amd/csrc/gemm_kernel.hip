@@ -39,8 +39,10 @@
 //     fragments are plain 16-byte LDS reads.  W is the MFMA's first operand
 //     and A the second: the accumulator block is then C^T, and each lane
 //     holds one row m of C with 4 consecutive columns n per block.
-//   * when K is a multiple of 128 the loads need no per-lane bound check:
-//     a piece's k offset and row step are the scalar offset of its load.
+//   * when K is a multiple of 128 the loads need no per-lane k check: a
+//     slice's k offset is the scalar offset of its loads.  A piece's row
+//     stays in the lane offset, which the buffer's range check covers (the
+//     scalar offset is not checked), so rows past M or N read as zero.
 //   * the bias is the accumulators' starting value, so the matrix cores add
 //     the products to it; the epilogue in registers applies GELU (erfc from
 //     Abramowitz and Stegun 7.1.26, rearranged so one form serves both
@@ -135,8 +137,9 @@ G_INLINE float activation(float z) {
 }
 
 // KFULL: K is a multiple of 2 * kBK, so every slice the loop computes lies
-// inside K and the loads need no per-lane bound check (the k offset of a
-// slice and the row step of a piece are the scalar offset of the load).
+// inside K and the loads need no per-lane k check (the k offset of a slice
+// is the scalar offset of the load; the row of a piece is in the lane
+// offset, where the range check sees it).
 template <int EPI, bool KFULL>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmParams p) {
@@ -191,14 +194,16 @@ gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t wrs = rsrc(p.w + (size_t)n0 * K, w_rows * (uint32_t)K * 2u);
   // Piece s of a wave covers rows row0 + 8 s: the swizzle term (row >> 1) & 7
   // then differs between even and odd s only (by 4), so two k offsets serve
-  // all pieces, and the row step is a scalar offset.
+  // all pieces.  The row of a piece stays in the lane offset (one register
+  // per piece): the buffer's range check covers the lane offset and not the
+  // scalar one, and rows past M or N must fall out of range.
   const int row0 = wave * kLoadsPerWave * 8 + (lane >> 3);
   int ld_k[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) ld_k[par] = 8 * ((lane & 7) ^ (((row0 >> 1) + 4 * par) & 7));
-  uint32_t ld_off[2];
+  uint32_t ld_off[kLoadsPerWave];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) ld_off[par] = (uint32_t)(row0 * K + ld_k[par]) * 2u;
+  for (int s = 0; s < kLoadsPerWave; ++s) ld_off[s] = (uint32_t)((row0 + 8 * s) * K + ld_k[s & 1]) * 2u;
   // A slice moves global -> VGPRs -> LDS: each wave loads its 8 pieces of
   // slice j+2 into registers during slice j and writes them to LDS during
   // slice j+1, so the loads spread over the slice and still have a slice of
@@ -210,8 +215,7 @@ gemm_kernel(GemmParams p) {
       // never used) are sent out of range through the lane offset, which is
       // what the buffer's range check covers, so nothing is read
       const bool in = k0 < K;
-      return __builtin_amdgcn_raw_buffer_load_b128(rs, in ? ld_off[s & 1] : kOut, in ? (uint32_t)(k0 + 8 * s * K) * 2u : 0u,
-                                                   0);
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, in ? ld_off[s] : kOut, in ? (uint32_t)k0 * 2u : 0u, 0);
     } else {
       const int k = k0 + ld_k[s & 1];
       const uint32_t off = k < K ? (uint32_t)((row0 + 8 * s) * K + k) * 2u : kOut;
@@ -451,16 +455,17 @@ gemm_kernel_small(GemmParams p) {
     lka[par] = 8 * ((lane & 7) ^ (((ra0 >> 1) + 4 * par) & 7));
     lkw[par] = 8 * ((lane & 7) ^ (((rw0 >> 1) + 4 * par) & 7));
   }
-  uint32_t loa[2], low[2];
+  // lane offset of each piece, its row included (the range check covers the
+  // lane offset only, and rows past M or N must fall out of range)
+  uint32_t loa[kSAPieces], low[kSWPieces];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    loa[par] = (uint32_t)(ra0 * K + lka[par]) * 2u;
-    low[par] = (uint32_t)(rw0 * K + lkw[par]) * 2u;
-  }
-  auto gload = [&](__amdgpu_buffer_rsrc_t rs, const uint32_t (&lo)[2], const int (&lk)[2], int row0, int s, int k0) -> u32x4 {
+  for (int s = 0; s < kSAPieces; ++s) loa[s] = (uint32_t)((ra0 + 8 * s) * K + lka[s & 1]) * 2u;
+#pragma unroll
+  for (int s = 0; s < kSWPieces; ++s) low[s] = (uint32_t)((rw0 + 8 * s) * K + lkw[s & 1]) * 2u;
+  auto gload = [&](__amdgpu_buffer_rsrc_t rs, const uint32_t* lo, const int (&lk)[2], int row0, int s, int k0) -> u32x4 {
     if constexpr (KFULL) {
       const bool in = k0 < K;
-      return __builtin_amdgcn_raw_buffer_load_b128(rs, in ? lo[s & 1] : kOut, in ? (uint32_t)(k0 + 8 * s * K) * 2u : 0u, 0);
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, in ? lo[s] : kOut, in ? (uint32_t)k0 * 2u : 0u, 0);
     } else {
       const int k = k0 + lk[s & 1];
       const uint32_t off = k < K ? (uint32_t)((row0 + 8 * s) * K + k) * 2u : kOut;
