@@ -746,8 +746,15 @@ gemm_kernel4(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // vmcnt(0) lgkmcnt(0) where the compiler sees it (0x70: expcnt left
+  // alone), so no read is pending across the loop's back edge and no step
+  // waits for the previous one's reads, then the barrier; scheduling fences
+  // keep every memory operation on its side
   auto sync = [&]() __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x70);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- main loop ---------------------------------------------------------------
@@ -755,7 +762,8 @@ gemm_kernel4(GemmParams p) {
   // fragments; then every wave waits for its pieces of slice s+1 and for the
   // others (barrier: buffer s % 2 is no longer read, slice s+1 has landed);
   // step 1 reads slice s+1's step-0 fragments and loads slice s+2 into
-  // buffer s % 2.
+  // buffer s % 2.  The loop runs from barrier to barrier (two slices an
+  // iteration), so nothing is in flight across its back edge.
   const int nk = K / kBK;   // even
 #pragma unroll
   for (int i = 0; i < 2 * k4Pieces; ++i) load_piece(i, 0, A0, W0);
@@ -767,14 +775,21 @@ gemm_kernel4(GemmParams p) {
   for (int r = 0; r < 8; ++r) af[0][r] = rda(A0, 0, r);
 #pragma unroll
   for (int r = 0; r < 8; ++r) wf[0][r] = rdw(W0, 0, r);
-  for (int s = 0; s < nk; s += 2) {
-    step(0, A0, W0, 1, false, 0, A0, W0);
+  step(0, A0, W0, 1, false, 0, A0, W0);   // slice 0, step 0
+  sync();
+  int s = 0;
+  for (; s + 2 < nk; s += 2) {
+    step(1, A1, W1, 0, true, s + 2, A0, W0);   // slice s, step 1
+    step(0, A1, W1, 1, false, 0, A1, W1);      // slice s+1, step 0
     sync();
-    step(1, A1, W1, 0, true, s + 2, A0, W0);
-    step(0, A1, W1, 1, false, 0, A1, W1);
+    step(1, A0, W0, 0, true, s + 3, A1, W1);   // slice s+1, step 1
+    step(0, A0, W0, 1, false, 0, A0, W0);      // slice s+2, step 0
     sync();
-    step(1, A0, W0, 0, true, s + 3, A1, W1);
   }
+  step(1, A1, W1, 0, true, s + 2, A0, W0);     // slice nk-2, step 1
+  step(0, A1, W1, 1, false, 0, A1, W1);        // slice nk-1, step 0
+  sync();
+  step(1, A0, W0, 0, false, 0, A1, W1);        // slice nk-1, step 1 (its reads are not used)
   // every wave is done with LDS: it takes the output
   __builtin_amdgcn_sched_barrier(0);
   sync();
