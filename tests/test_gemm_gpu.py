@@ -120,6 +120,17 @@ def test_ragged_tiles_without_k_checks(M, N, K):
            f"{M}x{N}x{K} ragged, no k checks")
 
 
+def test_four_wave_kernel_every_element():
+    """272 tiles of 256 x 256 with K a multiple of 128 (the 4-wave kernel
+    that runs the MLP workload), ragged in M and N, K = 384 (its loop runs
+    twice, then its tail): every element against the oracle."""
+    M, N, K = 16 * 256 + 3, 16 * 256 - 8, 384
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=31)
+    c = _run(a, w, b, EPI_BIAS_GELU)
+    _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
+           f"{M}x{N}x{K} every element, 4-wave kernel")
+
+
 def test_gelu_range_and_large_values():
     """Pre-activations from -40 to 40 (scaled weights): both GELU tails and the
     region around 0, where GELU bends, are exercised."""
