@@ -120,12 +120,15 @@ def test_ragged_tiles_without_k_checks(M, N, K):
            f"{M}x{N}x{K} ragged, no k checks")
 
 
-def test_four_wave_kernel_every_element():
-    """272 tiles of 256 x 256 with K a multiple of 128 (the 4-wave kernel
-    that runs the MLP workload), ragged in M and N, K = 384 (its loop runs
-    twice, then its tail): every element against the oracle."""
-    M, N, K = 16 * 256 + 3, 16 * 256 - 8, 384
-    a, w, b = synth.make_gemm_inputs(M, N, K, seed=31)
+@pytest.mark.parametrize("K", [384, 320, 64, 200, 72])
+def test_four_wave_kernel_every_element(K):
+    """272 tiles of 256 x 256, ragged in M and N.  K = 384 (an even number
+    of 64-wide slices: the 4-wave kernel's loop runs twice, then its tail),
+    320 and 64 (an odd number, rounded up by a slice of zeros) run the 4-wave
+    kernel, which runs the MLP workload; K = 200 and 72 (not multiples of 64)
+    the 8-wave kernel.  Every element against the oracle."""
+    M, N = 16 * 256 + 3, 16 * 256 - 8
+    a, w, b = synth.make_gemm_inputs(M, N, K, seed=31 + K)
     c = _run(a, w, b, EPI_BIAS_GELU)
     _check(c, synth.bits_to_f64(a, "bf16"), synth.bits_to_f64(w, "bf16"), b.astype(np.float64), EPI_BIAS_GELU,
            f"{M}x{N}x{K} every element, 4-wave kernel")

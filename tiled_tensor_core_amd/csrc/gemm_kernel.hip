@@ -13,7 +13,7 @@
 // fragment reads, swizzle, accumulation order and epilogue, so C is the same
 // bit for bit whichever runs:
 //   * gemm_kernel4, for problems of at least 256 tiles of 256 x 256 with K a
-//     multiple of 128: one workgroup of 4 waves per CU, one wave per SIMD,
+//     multiple of 64: one workgroup of 4 waves per CU, one wave per SIMD,
 //     128 x 128 of the tile per wave (8 x 8 MFMA blocks, 256 accumulators a
 //     lane in the accumulation registers).  The operand slices reach LDS
 //     straight from memory (buffer_load ... lds), so a k32 step issues only
@@ -614,7 +614,9 @@ gemm_kernel_small(GemmParams p) {
 // v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators a lane, one wave per SIMD).
 // The operand slices (k 64) reach LDS straight from memory (buffer_load ...
 // lds, no VGPR staging), double-buffered; one barrier per slice.  K must be a
-// multiple of 2 * kBK.
+// multiple of kBK, so no k chunk of a loaded slice lies past K and the loads
+// need no per-lane k check (a check in every load measured 5 % slower than
+// the 8-wave kernel on K = 4104: the 4-wave loop has no VALU to hide it).
 constexpr int k4Waves = 4;
 constexpr int k4Pieces = kSliceBytes / (k4Waves * 1024);   // 8 pieces of 1 KiB per operand per wave
 
@@ -681,23 +683,26 @@ gemm_kernel4(GemmParams p) {
   const u32x4 wrs = rsrc4(p.w + (size_t)n0 * K, w_rows * (uint32_t)K * 2u);
   const u32x4 ars0 = (u32x4){ars[0], ars[1], 0u, ars[3]};   // no bytes: every load out of range
   const u32x4 wrs0 = (u32x4){wrs[0], wrs[1], 0u, wrs[3]};
+  // (the logical chunk differs between even and odd pieces only)
   uint32_t loff[k4Pieces];
+  int lk[2];
   {
     const int row0 = wave * k4Pieces * 8 + (lane >> 3);
 #pragma unroll
-    for (int q = 0; q < k4Pieces; ++q) {
-      const int row = row0 + 8 * q;
-      loff[q] = (uint32_t)(row * K + 8 * ((lane & 7) ^ ((row >> 1) & 7))) * 2u;
-    }
+    for (int par = 0; par < 2; ++par) lk[par] = 8 * ((lane & 7) ^ (((row0 >> 1) + 4 * par) & 7));
+#pragma unroll
+    for (int q = 0; q < k4Pieces; ++q) loff[q] = (uint32_t)((row0 + 8 * q) * K + lk[q & 1]) * 2u;
   }
   const int wofs = wave * k4Pieces * 1024;
   // piece i of 16 (0-7 A, 8-15 W) of slice s into the buffers ab / wb
   auto load_piece = [&](int i, int s, lds_u8* ab, lds_u8* wb) __attribute__((always_inline)) {
     const bool in = s * kBK < K;
+    const int q = i % k4Pieces;
+    const uint32_t off = loff[q];
     if (i < k4Pieces)
-      load_lds(in ? ars : ars0, ab + wofs + i * 1024, loff[i], (uint32_t)(s * kBK) * 2u);
+      load_lds(in ? ars : ars0, ab + wofs + q * 1024, off, (uint32_t)(s * kBK) * 2u);
     else
-      load_lds(in ? wrs : wrs0, wb + wofs + (i - k4Pieces) * 1024, loff[i - k4Pieces], (uint32_t)(s * kBK) * 2u);
+      load_lds(in ? wrs : wrs0, wb + wofs + q * 1024, off, (uint32_t)(s * kBK) * 2u);
   };
 
   // ---- fragment reads: lane l reads row l % 16 of a 16-row block, k chunk
@@ -763,8 +768,10 @@ gemm_kernel4(GemmParams p) {
   // others (barrier: buffer s % 2 is no longer read, slice s+1 has landed);
   // step 1 reads slice s+1's step-0 fragments and loads slice s+2 into
   // buffer s % 2.  The loop runs from barrier to barrier (two slices an
-  // iteration), so nothing is in flight across its back edge.
-  const int nk = K / kBK;   // even
+  // iteration), so nothing is in flight across its back edge.  The slice
+  // count is rounded up to even (a slice past K reads as zeros and adds
+  // exactly nothing), so the loop and its tail are one code path.
+  const int nk = ((K + kBK - 1) / kBK + 1) & ~1;
 #pragma unroll
   for (int i = 0; i < 2 * k4Pieces; ++i) load_piece(i, 0, A0, W0);
 #pragma unroll
@@ -866,9 +873,9 @@ hipError_t launch_gemm(int epi, const GemmParams& prm, hipStream_t stream) {
     return hipGetLastError();
   }
   const bool kfull = p.K % (2 * kBK) == 0;
-  if (kfull && big_tiles >= 256) {
-    // at least one tile per CU and K a multiple of 128: the 4-wave kernel
-    // (measured 3-4 % faster from 256 tiles up, 6 % slower at 144)
+  if (big_tiles >= 256 && p.K % kBK == 0) {
+    // at least one tile per CU and K a multiple of 64: the 4-wave kernel
+    // (measured 3-5 % faster from 256 tiles up, 6 % slower at 144)
     const dim3 block4(k4Waves * 64);
     switch (epi) {
       case 0: hipLaunchKernelGGL((gemm_kernel4<0>), grid, block4, 0, stream, p); break;
